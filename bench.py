@@ -1,0 +1,221 @@
+"""Benchmark of the owner-local Muon + AdamW-tail step on one MI355X.
+
+One step = mfsdp_muon_step over every owned matrix of the workload (momentum,
+Nesterov, Frobenius normalization, 5 quintic Newton-Schulz iterations, apply)
+followed by mfsdp_adamw_tail over the packed tail, on one HIP stream, with all
+inputs resident in HBM.  W warm-up steps, then exactly K timed steps between
+two device synchronizations.
+
+Prints one JSON line.  ``value`` is the Newton-Schulz algorithmic TFLOP/s of
+the whole step (NS flops per step / wall time per step); ``ms_per_step`` is
+the step time.  ``roofline`` describes the dominant kernel (most GPU time per
+step), timed with hipEvents recorded by the library around each of its
+launches on the launch stream inside the timed region.  ``cpu_baseline`` is
+the float64 oracle on a bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+METRIC = "owner-local Muon step ms and Newton-Schulz TFLOP/s (% bf16 MFMA peak)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+KINDS = ("momentum", "norm", "gram", "poly", "update", "apply", "adamw")
+
+
+def ns_flops_by_kind(shapes):
+    """Algorithmic flops of ONE launch of each Newton-Schulz kernel kind.
+
+    With m = min(r, c), n = max(r, c): gram A = X X^T counts its upper triangle
+    m(m+1)n; poly A A the same way m^2(m+1); update B X 2 m^2 n.
+    """
+    g = p = u = 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        g += m * (m + 1) * n
+        p += m * m * (m + 1)
+        u += 2 * m * m * n
+    return {"gram": g, "poly": p, "update": u}
+
+
+def elementwise_bytes(shapes, es, tail_n):
+    """Algorithmic HBM bytes of one launch of the elementwise kernels."""
+    elems = sum(r * c for r, c in shapes)
+    return {"momentum": elems * 4 * es,      # read G, M; write M', U
+            "adamw": tail_n * 7 * 4}         # read p, g, m, v; write p, m, v
+
+
+def cpu_baseline(key, budget_s=20.0):
+    """Time the float64 oracle on a bounded sample of the workload."""
+    import oracle
+    from matrix_optimizer_step_owner_amd import workloads as wlm
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    wl = wlm.WORKLOADS[key]
+    # smallest-first distinct shapes until the budget is spent
+    order = sorted(range(len(wl.matrices)),
+                   key=lambda i: ns_flops_by_kind([(wl.matrices[i].rows,
+                                                    wl.matrices[i].cols)])["update"])
+    inp = wlm.generate(key, seed=0, matrix_indices=order[:8])
+    idx_map = {i: k for k, i in enumerate(sorted(order[:8]))}
+    done_flops = 0
+    done = []
+    t_total = 0.0
+    for i in order[:8]:
+        k = idx_map[i]
+        W, G, M = (t.double().numpy() for t in (inp.weights[k], inp.grads[k], inp.momenta[k]))
+        t0 = time.perf_counter()
+        oracle.muon_matrix_step(W, G, M, lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov,
+                                weight_decay=wl.weight_decay, ns_steps=wl.ns_steps,
+                                abc=wl.abc)
+        t_total += time.perf_counter() - t0
+        f = ns_flops_by_kind([(wl.matrices[i].rows, wl.matrices[i].cols)])
+        done_flops += wl.ns_steps * sum(f.values())
+        done.append(f"{wl.matrices[i].rows}x{wl.matrices[i].cols}")
+        if t_total > budget_s:
+            break
+    return {"value": done_flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle Muon step on {len(done)} matrices of "
+                      f"{key} ({', '.join(done)}), {t_total:.1f} s, NS algorithmic flops "
+                      f"{done_flops:.3e}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="block_d2048")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the owner-local step on one GPU only; "
+              "--gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import matrix_optimizer_step_owner_amd as mf
+    from matrix_optimizer_step_owner_amd import workloads as wlm
+
+    dev = torch.device("cuda:0")
+    wl = wlm.WORKLOADS[args.workload]
+    inp = wlm.generate(args.workload, seed=0)
+    shapes = [(s.rows, s.cols) for s in wl.matrices]
+    W = [t.to(dev) for t in inp.weights]
+    G = [t.to(dev) for t in inp.grads]
+    M = [t.to(dev) for t in inp.momenta]
+    P, Gt, Mt, Vt = (t.to(dev) for t in (inp.tail_p, inp.tail_g, inp.tail_m, inp.tail_v))
+    del inp
+    es = 2 if wl.dtype == torch.bfloat16 else 4
+    ws = torch.empty(mf.muon_workspace_size(shapes, wl.dtype), dtype=torch.uint8, device=dev)
+    hp = dict(lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov, weight_decay=wl.weight_decay,
+              ns_steps=wl.ns_steps, abc=wl.abc)
+
+    def step():
+        mf.muon_step(W, G, M, workspace=ws, **hp)
+        mf.adamw_tail(P, Gt, Mt, Vt, lr=wl.adam_lr, beta1=wl.adam_beta1,
+                      beta2=wl.adam_beta2, eps=wl.adam_eps,
+                      weight_decay=wl.adam_weight_decay, step=wl.adam_step)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    mf.timing.reset()
+    mf.timing.enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    mf.timing.enable(False)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_kind = {}
+    for k in KINDS:
+        tot, cnt = mf.timing.read(k)
+        if cnt:
+            per_kind[k] = {"avg_ms": tot / cnt, "launches": cnt,
+                           "ms_per_step": tot / args.steps}
+
+    flops = ns_flops_by_kind(shapes)
+    ns_flops_step = wl.ns_steps * sum(flops.values())
+    ns_kernel_ms = sum(per_kind[k]["ms_per_step"] for k in ("gram", "poly", "update")
+                       if k in per_kind)
+    peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_FP32_MFMA_TFLOPS
+    dominant = max(per_kind, key=lambda k: per_kind[k]["ms_per_step"])
+    ew = elementwise_bytes(shapes, es, wl.tail_n)
+    if dominant in flops:
+        achieved = flops[dominant] / (per_kind[dominant]["avg_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+    else:
+        achieved = ew[dominant] / (per_kind[dominant]["avg_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    roof["kernel"] = dominant
+    roof["traffic"] = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        if tr.get("kernel") == dominant and tr.get("workload") == args.workload:
+            roof["traffic"] = tr.get("bytes_per_launch")
+
+    kernels = {}
+    for k, v in per_kind.items():
+        e = {"avg_ms": round(v["avg_ms"], 5), "ms_per_step": round(v["ms_per_step"], 5)}
+        if k in flops:
+            e["tflops"] = round(flops[k] / (v["avg_ms"] * 1e-3) / 1e12, 2)
+        if k in ew:
+            e["gbs"] = round(ew[k] / (v["avg_ms"] * 1e-3) / 1e9, 1)
+        kernels[k] = e
+
+    out = {
+        "metric": METRIC,
+        "value": round(ns_flops_step / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "matrices": len(shapes),
+                   "elements": wl.n_elements, "tail": wl.tail_n, "ns_steps": wl.ns_steps,
+                   "ns_flops_per_step": ns_flops_step},
+        "ns_tflops_kernels": round(ns_flops_step / (ns_kernel_ms * 1e-3) / 1e12, 2)
+        if ns_kernel_ms else None,
+        "pct_bf16_peak_step": round(100 * ns_flops_step / (ms_per_step * 1e-3) / 1e12 / peak, 2),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.workload,
+                                                                      args.cpu_budget),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * mfsdp.h -- C ABI of the owner-local optimizer step on MI355X (gfx950).
+ *
+ * Source of the operations: "MatrixFSDP: communication-free matrix optimizers
+ * under ZeRO-3 parameter sharding" (arxivlens page, Abstract; gist.science
+ * technical summaries, section "Methodologie", part 1 "owner-shaped
+ * placement").  Under owner-shaped ZeRO-3 placement every 2D weight lives whole
+ * on one data-parallel owner and every other rank holds an empty shard for it;
+ * after the ordinary gradient reduction the owner holds the whole gradient, so
+ * its Muon step -- momentum, Newton-Schulz orthogonalization of the whole
+ * matrix, update -- involves no communication.  Non-matrix tensors are packed
+ * into tail owners and keep AdamW.  This library is that step on one GPU:
+ *
+ *   mfsdp_muon_step   -- Muon on the owner's list of whole matrices,
+ *   mfsdp_adamw_tail  -- AdamW on a packed fp32 tail buffer.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer named "device" is a device (HBM) address on the current
+ *     HIP device.  The caller owns every buffer; the library never allocates
+ *     or frees device memory.  Host pointers are read only during the call.
+ *   - Work is enqueued asynchronously on `stream`; no call synchronizes the
+ *     host with the device.
+ *   - All arguments are validated before anything is enqueued.  On any
+ *     status other than MFSDP_OK nothing has been modified, except for
+ *     MFSDP_ERR_HIP, which is returned when the HIP runtime fails after work
+ *     was enqueued (the contents of the outputs are then undefined).
+ *   - mfsdp_last_error() returns a thread-local description of the last
+ *     failure on the calling thread.  No C++ exception crosses this ABI.
+ *   - Non-finite inputs are not checked: they propagate to the outputs.
+ */
+#ifndef MFSDP_H_
+#define MFSDP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mfsdp_status {
+  MFSDP_OK = 0,
+  MFSDP_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad scalar    */
+  MFSDP_ERR_UNSUPPORTED = 2,      /* dtype or size this build cannot run   */
+  MFSDP_ERR_WORKSPACE = 3,        /* workspace too small or misaligned     */
+  MFSDP_ERR_ALIAS = 4,            /* two buffers that must not overlap do  */
+  MFSDP_ERR_HIP = 5               /* the HIP runtime reported an error     */
+} mfsdp_status_t;
+
+typedef enum mfsdp_dtype {
+  MFSDP_DTYPE_F32 = 0,  /* W, G, M and the Newton-Schulz iterates in fp32    */
+  MFSDP_DTYPE_BF16 = 1  /* W, G, M in bf16; NS iterates bf16, fp32 accumulate */
+} mfsdp_dtype_t;
+
+/* Additive guard of the Frobenius normalization X0 = U / (||U||_F + eps). */
+#define MFSDP_NS_EPS 1e-7f
+
+/* Byte alignment required of every device buffer and of the workspace. */
+#define MFSDP_ALIGNMENT 16
+
+/*
+ * One whole matrix owned by this rank (arxivlens Abstract: the owner holds the
+ * complete 2D weight; its gradient arrives whole after the backward
+ * reduction).  Stored row-major as rows x cols (rows = out_features),
+ * contiguous, in the call's dtype.
+ *
+ *   weight      device, rows*cols, updated in place:
+ *                 W <- (1 - lr*weight_decay) * W - lr * scale * O
+ *   grad        device, rows*cols, read only
+ *   momentum    device, rows*cols, updated in place: M <- beta*M + G
+ *   update_out  device fp32 rows*cols, or NULL.  When given it receives O, the
+ *               orthogonalized update before lr and scale.
+ *   scale       the per-matrix update scale s (> 0, finite).  The common
+ *               convention is sqrt(max(1, rows/cols)); the pages fix none.
+ */
+typedef struct mfsdp_matrix {
+  void* weight;
+  const void* grad;
+  void* momentum;
+  float* update_out;
+  int64_t rows;
+  int64_t cols;
+  float scale;
+} mfsdp_matrix_t;
+
+/*
+ * Workspace bytes that mfsdp_muon_step needs for this list (host call, no
+ * device access).  The workspace holds the Newton-Schulz iterates of every
+ * matrix (two m_pad x n_pad buffers and two m_pad x m_pad buffers per matrix,
+ * m = min(rows, cols), n = max(rows, cols), padded to the 256-wide tile), the
+ * per-block partial sums of the Frobenius norm and the launch descriptors.
+ * Only rows, cols are read from `mats`.  n_mats == 0 gives 0 bytes.
+ * Errors: MFSDP_ERR_INVALID_ARGUMENT (null out / mats with n_mats > 0,
+ * non-positive dims), MFSDP_ERR_UNSUPPORTED (dtype, or a size beyond the
+ * 32-bit element indexing of the kernels).
+ */
+mfsdp_status_t mfsdp_muon_workspace_size(const mfsdp_matrix_t* mats,
+                                         int64_t n_mats, mfsdp_dtype_t dtype,
+                                         size_t* out_bytes);
+
+/*
+ * Owner-local Muon step over `n_mats` whole matrices (host array `mats`).
+ *
+ * For each matrix, in fp32 arithmetic (arxivlens Abstract: Muon orthogonalizes
+ * momentum-smoothed updates with Newton-Schulz on the whole matrix):
+ *   M' = beta*M + G                                  (stored to momentum)
+ *   U  = G + beta*M'   (nesterov != 0)   or   U = M'
+ *   X0 = U / (||U||_F + MFSDP_NS_EPS), transposed to m x n when rows > cols
+ *   ns_steps times:  A = X X^T;  B = b*A + c*A*A;  X = a*X + B*X
+ *   O  = X (transposed back)
+ *   W' = (1 - lr*weight_decay)*W - lr*scale*O        (stored to weight)
+ * With dtype BF16, X, A and B are rounded to bf16 (round to nearest even)
+ * between the products, which accumulate in fp32.  Matrices are independent:
+ * results do not depend on their order in the list or on how the library
+ * groups them.
+ *
+ * workspace        device, >= mfsdp_muon_workspace_size bytes, 256-byte
+ *                  aligned; contents are scratch and are overwritten.
+ * n_mats == 0      (a rank that owns no matrix) returns MFSDP_OK, no work.
+ * Validation: non-null weight/grad/momentum, rows, cols >= 1, 16-byte
+ * aligned buffers, pairwise non-overlapping weight/grad/momentum/update_out/
+ * workspace across the whole list, ns_steps in [0, 100], finite lr, beta,
+ * weight_decay, a, b, c and scale, scale > 0.
+ */
+mfsdp_status_t mfsdp_muon_step(const mfsdp_matrix_t* mats, int64_t n_mats,
+                               mfsdp_dtype_t dtype, float lr, float beta,
+                               int nesterov, float weight_decay, int ns_steps,
+                               float a, float b, float c, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Decoupled AdamW on a packed fp32 tail of n elements (arxivlens Abstract:
+ * non-matrix tensors are packed into tail owners and stay on AdamW).
+ * Elementwise, with t = step (>= 1):
+ *   p  <- p * (1 - lr*weight_decay)
+ *   m  <- beta1*m + (1-beta1)*g
+ *   v  <- beta2*v + (1-beta2)*g*g
+ *   p  <- p - lr * (m / (1-beta1^t)) / (sqrt(v / (1-beta2^t)) + eps)
+ * param, exp_avg, exp_avg_sq are device fp32[n] updated in place, grad is
+ * device fp32[n] read only; all 16-byte aligned and non-overlapping.
+ * n == 0 (an owner with no tail) returns MFSDP_OK without touching the device.
+ * Validation: non-null pointers for n > 0, n >= 0, step >= 1, finite
+ * hyperparameters, beta1 and beta2 in [0, 1), eps >= 0.
+ */
+mfsdp_status_t mfsdp_adamw_tail(float* param, const float* grad,
+                                float* exp_avg, float* exp_avg_sq, int64_t n,
+                                float lr, float beta1, float beta2, float eps,
+                                float weight_decay, int64_t step,
+                                hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* mfsdp_status_string(mfsdp_status_t status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* mfsdp_last_error(void);
+
+/*
+ * Kernel timing for measurement tools.  Kernels of the library fall into the
+ * kinds below.  While timing is enabled on a thread, every launch that thread
+ * makes is bracketed by a pair of hipEvents recorded on the launch stream;
+ * mfsdp_timing_read synchronizes those events and returns, per kind, the
+ * summed milliseconds and the number of launches since the last reset.
+ * Events are created lazily by the library (no device-memory allocation) and
+ * kept per thread.  Not needed for normal use.
+ */
+typedef enum mfsdp_kernel_kind {
+  MFSDP_KERNEL_MOMENTUM = 0,  /* momentum + Nesterov + norm partials */
+  MFSDP_KERNEL_NORM = 1,      /* per-matrix norm finalization        */
+  MFSDP_KERNEL_GRAM = 2,      /* A = X X^T                           */
+  MFSDP_KERNEL_POLY = 3,      /* B = b A + c A A                     */
+  MFSDP_KERNEL_UPDATE = 4,    /* X = a X + B X (last one applies W)  */
+  MFSDP_KERNEL_APPLY = 5,     /* apply when ns_steps == 0            */
+  MFSDP_KERNEL_ADAMW = 6,     /* AdamW tail                          */
+  MFSDP_KERNEL_KINDS = 7
+} mfsdp_kernel_kind_t;
+
+mfsdp_status_t mfsdp_timing_enable(int enable);
+mfsdp_status_t mfsdp_timing_reset(void);
+mfsdp_status_t mfsdp_timing_read(mfsdp_kernel_kind_t kind, double* total_ms,
+                                 int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MFSDP_H_ */

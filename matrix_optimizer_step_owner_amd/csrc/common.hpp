@@ -1,0 +1,143 @@
+// Shared device-side helpers of the owner-local optimizer step (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mfsdp {
+
+// Newton-Schulz output tile (rows and columns) of the MFMA kernels; every
+// iterate buffer is padded to a multiple of it.
+constexpr int kTile = 256;
+// Tile edge of the elementwise momentum kernel (divides kTile).
+constexpr int kEwTile = 64;
+constexpr int kThreads = 256;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Element traits: storage type, elements per 16-byte vector, conversions.
+struct ElemBF16 {
+  using storage_t = uint16_t;
+  static constexpr int kVec = 8;
+  __device__ __forceinline__ static float load(const storage_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static float to_f32(storage_t s) { return bf16_to_f32(s); }
+  __device__ __forceinline__ static storage_t from_f32(float f) { return f32_to_bf16_rne(f); }
+};
+
+struct ElemF32 {
+  using storage_t = float;
+  static constexpr int kVec = 4;
+  __device__ __forceinline__ static float load(const storage_t* p) { return *p; }
+  __device__ __forceinline__ static float to_f32(storage_t s) { return s; }
+  __device__ __forceinline__ static storage_t from_f32(float f) { return f; }
+};
+
+// Unpack / pack a 16-byte vector of storage elements.
+template <class E>
+struct Vec16 {
+  static constexpr int N = E::kVec;
+  __device__ __forceinline__ static void unpack(const uint4& v, float (&out)[N]);
+  __device__ __forceinline__ static uint4 pack(const float (&in)[N]);
+};
+
+template <>
+struct Vec16<ElemBF16> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void unpack(const uint4& v, float (&out)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static uint4 pack(const float (&in)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16_rne(in[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16_rne(in[2 * i + 1])) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+template <>
+struct Vec16<ElemF32> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void unpack(const uint4& v, float (&out)[4]) {
+    out[0] = __uint_as_float(v.x);
+    out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z);
+    out[3] = __uint_as_float(v.w);
+  }
+  __device__ __forceinline__ static uint4 pack(const float (&in)[4]) {
+    return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]),
+                      __float_as_uint(in[2]), __float_as_uint(in[3]));
+  }
+};
+
+// Per-matrix device descriptor, written by the host into the workspace.
+// "Wide" coordinates (i < m, j < n) index the Newton-Schulz iterate; a tall
+// matrix (rows > cols) maps wide (i, j) to stored (j, i).
+struct MatDesc {
+  void* W;            // rows x cols, storage dtype
+  const void* G;      // rows x cols
+  void* M;            // rows x cols
+  float* upd;         // rows x cols fp32 or null
+  void* X0;           // m_pad x n_pad: U, then even iterates
+  void* X1;           // m_pad x n_pad: odd iterates
+  void* A;            // m_pad x m_pad: X X^T
+  void* B;            // m_pad x m_pad: b A + c A A
+  int32_t rows, cols;
+  int32_t m, n, m_pad, n_pad;
+  int32_t tall;
+  int32_t ew_tile0;   // first momentum-kernel tile of this matrix
+  int32_t ew_tiles_j; // momentum-kernel tiles along the wide n axis
+  int32_t ew_ntiles;  // momentum-kernel tiles of this matrix
+  float lr_scale;     // lr * scale
+  int32_t vec_ok;     // rows of W/G/M/upd start 16-byte aligned
+};
+
+// Grouped launch: work item p covers tiles [begin[p], begin[p+1]) of matrix
+// mat[p].  Each workgroup finds its item by binary search.
+struct WorkList {
+  const int32_t* mat;
+  const int32_t* begin;  // n_items + 1 entries
+  int32_t n_items;
+};
+
+__device__ __forceinline__ int find_item(const WorkList& wl, int32_t bid) {
+  int lo = 0, hi = wl.n_items - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (wl.begin[mid] <= bid) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ double warp_sum(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace mfsdp

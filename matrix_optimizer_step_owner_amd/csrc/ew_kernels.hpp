@@ -1,0 +1,201 @@
+// Elementwise kernels of the owner-local step: momentum + Nesterov + norm
+// partials (written in the wide Newton-Schulz layout), per-matrix norm
+// finalization, the apply used when no Newton-Schulz iteration runs, and the
+// AdamW tail.  All are HBM-bound; loads and stores are 16-byte vectors where
+// the row alignment allows it.
+#pragma once
+
+#include "common.hpp"
+
+namespace mfsdp {
+
+// Momentum M' = beta*M + G, Nesterov U = G + beta*M' (or U = M'), sum of U^2
+// per tile, and U stored into X0 in wide layout (transposed when rows > cols),
+// zero in the tile padding.  One 256-thread workgroup per 64x64 wide tile.
+template <class E>
+__global__ __launch_bounds__(kThreads) void momentum_kernel(
+    const MatDesc* __restrict__ descs, WorkList wl, double* __restrict__ partials,
+    float beta, int nesterov) {
+  using S = typename E::storage_t;
+  constexpr int V = E::kVec;
+  constexpr int T = kEwTile;
+  __shared__ float sU[T][T + 1];
+  __shared__ float sRed[kThreads / 64];
+
+  const int bid = blockIdx.x;
+  const int item = find_item(wl, bid);
+  const MatDesc d = descs[wl.mat[item]];
+  const int local = bid - wl.begin[item];
+  const int ti = local / d.ew_tiles_j, tj = local % d.ew_tiles_j;
+  const int i0 = ti * T, j0 = tj * T;          // wide tile origin
+  const int sr0 = d.tall ? j0 : i0;            // stored-layout tile origin
+  const int sc0 = d.tall ? i0 : j0;
+  const int tid = threadIdx.x;
+
+  const S* G = static_cast<const S*>(d.G);
+  S* M = static_cast<S*>(d.M);
+  float ssq = 0.f;
+
+  if (d.vec_ok) {
+    constexpr int VPR = T / V;                 // vectors per tile row
+    for (int e = tid; e < T * VPR; e += kThreads) {
+      const int r = e / VPR, cv = e % VPR;
+      const int sr = sr0 + r, sc = sc0 + cv * V;
+      float u[V];
+      if (sr < d.rows && sc < d.cols) {
+        const size_t off = static_cast<size_t>(sr) * d.cols + sc;
+        float g[V], mo[V], mn[V];
+        Vec16<E>::unpack(*reinterpret_cast<const uint4*>(G + off), g);
+        Vec16<E>::unpack(*reinterpret_cast<const uint4*>(M + off), mo);
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          mn[k] = fmaf(beta, mo[k], g[k]);
+          u[k] = nesterov ? fmaf(beta, mn[k], g[k]) : mn[k];
+          ssq = fmaf(u[k], u[k], ssq);
+        }
+        *reinterpret_cast<uint4*>(M + off) = Vec16<E>::pack(mn);
+      } else {
+#pragma unroll
+        for (int k = 0; k < V; ++k) u[k] = 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < V; ++k) sU[r][cv * V + k] = u[k];
+    }
+  } else {
+    for (int e = tid; e < T * T; e += kThreads) {
+      const int r = e / T, cc = e % T;
+      const int sr = sr0 + r, sc = sc0 + cc;
+      float u = 0.f;
+      if (sr < d.rows && sc < d.cols) {
+        const size_t off = static_cast<size_t>(sr) * d.cols + sc;
+        const float g = E::load(G + off);
+        const float mn = fmaf(beta, E::load(M + off), g);
+        u = nesterov ? fmaf(beta, mn, g) : mn;
+        ssq = fmaf(u, u, ssq);
+        M[off] = E::from_f32(mn);
+      }
+      sU[r][cc] = u;
+    }
+  }
+  __syncthreads();
+
+  // Store U into X0 (wide layout, rows 16-byte aligned, padding included).
+  S* X0 = static_cast<S*>(d.X0);
+  constexpr int VPR = T / V;
+  for (int e = tid; e < T * VPR; e += kThreads) {
+    const int ii = e / VPR, jv = e % VPR;
+    float u[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) u[k] = d.tall ? sU[jv * V + k][ii] : sU[ii][jv * V + k];
+    const size_t off = static_cast<size_t>(i0 + ii) * d.n_pad + j0 + jv * V;
+    *reinterpret_cast<uint4*>(X0 + off) = Vec16<E>::pack(u);
+  }
+
+  // Deterministic block reduction of the sum of squares.
+  ssq = warp_sum(ssq);
+  if ((tid & 63) == 0) sRed[tid >> 6] = ssq;
+  __syncthreads();
+  if (tid == 0) {
+    double s = 0.0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) s += static_cast<double>(sRed[w]);
+    partials[d.ew_tile0 + local] = s;
+  }
+}
+
+// scale[k] = 1 / (sqrt(sum of matrix k's partials) + eps), summed in a fixed
+// order.  One workgroup per matrix.
+__global__ __launch_bounds__(kThreads) void norm_finalize_kernel(
+    const MatDesc* __restrict__ descs, const double* __restrict__ partials,
+    float* __restrict__ scales, float eps) {
+  __shared__ double sRed[kThreads / 64];
+  const MatDesc d = descs[blockIdx.x];
+  double s = 0.0;
+  for (int t = threadIdx.x; t < d.ew_ntiles; t += kThreads) s += partials[d.ew_tile0 + t];
+  s = warp_sum(s);
+  if ((threadIdx.x & 63) == 0) sRed[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) tot += sRed[w];
+    scales[blockIdx.x] = static_cast<float>(1.0 / (sqrt(tot) + static_cast<double>(eps)));
+  }
+}
+
+// Apply with no Newton-Schulz iteration: O = s * U, W <- decay*W - lr*scale*O.
+template <class E>
+__global__ __launch_bounds__(kThreads) void apply_x0_kernel(
+    const MatDesc* __restrict__ descs, WorkList wl, const float* __restrict__ scales,
+    float decay) {
+  using S = typename E::storage_t;
+  constexpr int T = kEwTile;
+  const int bid = blockIdx.x;
+  const int item = find_item(wl, bid);
+  const int k = wl.mat[item];
+  const MatDesc d = descs[k];
+  const int local = bid - wl.begin[item];
+  const int i0 = (local / d.ew_tiles_j) * T, j0 = (local % d.ew_tiles_j) * T;
+  const float s = scales[k];
+  const S* X0 = static_cast<const S*>(d.X0);
+  S* W = static_cast<S*>(d.W);
+  for (int e = threadIdx.x; e < T * T; e += kThreads) {
+    const int i = i0 + e / T, j = j0 + e % T;
+    if (i >= d.m || j >= d.n) continue;
+    const float o = s * E::to_f32(X0[static_cast<size_t>(i) * d.n_pad + j]);
+    const size_t off = d.tall ? static_cast<size_t>(j) * d.cols + i
+                              : static_cast<size_t>(i) * d.cols + j;
+    W[off] = E::from_f32(fmaf(-d.lr_scale, o, decay * E::to_f32(W[off])));
+    if (d.upd) d.upd[off] = o;
+  }
+}
+
+// Decoupled AdamW on a packed fp32 buffer; 16-byte vectors over n/4 groups,
+// the n%4 remainder by the first threads.
+struct AdamWArgs {
+  float decay;       // 1 - lr*wd
+  float beta1, beta2;
+  float one_m_beta1, one_m_beta2;
+  float step_size;   // lr / (1 - beta1^t)
+  float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
+  float eps;
+};
+
+__device__ __forceinline__ void adamw_elem(float& p, float g, float& m, float& v,
+                                           const AdamWArgs& a) {
+  m = fmaf(a.beta1, m, a.one_m_beta1 * g);
+  v = fmaf(a.beta2, v, a.one_m_beta2 * g * g);
+  const float denom = fmaf(sqrtf(v), a.inv_sqrt_bc2, a.eps);
+  p = fmaf(-a.step_size, m / denom, p * a.decay);
+}
+
+__global__ __launch_bounds__(kThreads) void adamw_kernel(
+    float* __restrict__ p, const float* __restrict__ g, float* __restrict__ m,
+    float* __restrict__ v, int64_t n, AdamWArgs a) {
+  const int64_t n4 = n >> 2;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t q = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; q < n4;
+       q += stride) {
+    float4 pp = reinterpret_cast<float4*>(p)[q];
+    const float4 gg = reinterpret_cast<const float4*>(g)[q];
+    float4 mm = reinterpret_cast<float4*>(m)[q];
+    float4 vv = reinterpret_cast<float4*>(v)[q];
+    adamw_elem(pp.x, gg.x, mm.x, vv.x, a);
+    adamw_elem(pp.y, gg.y, mm.y, vv.y, a);
+    adamw_elem(pp.z, gg.z, mm.z, vv.z, a);
+    adamw_elem(pp.w, gg.w, mm.w, vv.w, a);
+    reinterpret_cast<float4*>(p)[q] = pp;
+    reinterpret_cast<float4*>(m)[q] = mm;
+    reinterpret_cast<float4*>(v)[q] = vv;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+    const int64_t i = (n4 << 2) + threadIdx.x;
+    float pp = p[i], mm = m[i], vv = v[i];
+    adamw_elem(pp, g[i], mm, vv, a);
+    p[i] = pp;
+    m[i] = mm;
+    v[i] = vv;
+  }
+}
+
+}  // namespace mfsdp

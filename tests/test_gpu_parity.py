@@ -1,0 +1,196 @@
+"""GPU parity of the HIP owner-local step against the float64 oracle.
+
+Every test runs the library through its C ABI (Python ctypes binding) on
+cuda:0 and compares with ``oracle`` on the same host values.  Bars: see
+tests/gpu_helpers.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import matrix_optimizer_step_owner_amd as mf
+from matrix_optimizer_step_owner_amd import workloads as wlm
+import oracle
+
+from gpu_helpers import (ADAMW_TOL, BF16_TOL, F32_TOL, GpuStep, check_matrix,
+                         f64, muon_hparams, oracle_matrix, rel, run_and_check, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# ---------------------------------------------------------------------------
+# AdamW tail
+# ---------------------------------------------------------------------------
+
+def adamw_check(p, g, m, v, step, lr=0.02, beta1=0.9, beta2=0.95, eps=1e-8, wd=0.01,
+                label=""):
+    dev = torch.device("cuda:0")
+    P, Gd, Md, Vd = (t.to(dev) for t in (p, g, m, v))
+    mf.adamw_tail(P, Gd, Md, Vd, lr=lr, beta1=beta1, beta2=beta2, eps=eps,
+                  weight_decay=wd, step=step)
+    torch.cuda.synchronize()
+    pr, mr, vr = oracle.adamw_tail(f64(p), f64(g), f64(m), f64(v), lr=lr, beta1=beta1,
+                                   beta2=beta2, eps=eps, weight_decay=wd, step=step)
+    ep, em, ev = rel(f64(P), pr), rel(f64(Md), mr), rel(f64(Vd), vr)
+    edp = rel(f64(P) - f64(p), pr - f64(p))
+    say(f"adamw {label} n={p.numel()} t={step}: rel p={ep:.2e} m={em:.2e} v={ev:.2e} "
+        f"(dp {edp:.2e})")
+    assert ep <= ADAMW_TOL and em <= ADAMW_TOL and ev <= ADAMW_TOL
+
+
+@pytest.mark.parametrize("key", ["tiny_fp32", "block_d2048", "llama3_8b_4blocks",
+                                 "d5120_2blocks"])
+def test_adamw_workload_tails(key):
+    wl = wlm.WORKLOADS[key]
+    rng = np.random.default_rng(0)
+    p, g, m, v = wlm.draw_tail(rng, wl)
+    adamw_check(p, g, m, v, wl.adam_step, lr=wl.adam_lr, beta1=wl.adam_beta1,
+                beta2=wl.adam_beta2, eps=wl.adam_eps, wd=wl.adam_weight_decay, label=key)
+
+
+@pytest.mark.parametrize("n", [1, 3, 5, 255, 1023, 4097, 1 << 20])
+def test_adamw_ragged_and_warm_state(n):
+    p, g, m, v = wlm.random_tail_state(n, seed=n)
+    adamw_check(p, g, m, v, step=10, label="warm")
+
+
+def test_adamw_empty_tail():
+    z = torch.zeros(0, device="cuda:0")
+    mf.adamw_tail(z, z, z, z, lr=0.02, step=1)
+
+
+# ---------------------------------------------------------------------------
+# Muon: small cases against the oracle
+# ---------------------------------------------------------------------------
+
+def test_tiny_fp32_workload():
+    inp = wlm.generate("tiny_fp32", seed=0)
+    hp = muon_hparams(inp.workload)
+    run_and_check(inp.weights, inp.grads, inp.momenta, hp, torch.float32, label="tiny")
+    wl = inp.workload
+    adamw_check(inp.tail_p, inp.tail_g, inp.tail_m, inp.tail_v, 1, lr=wl.adam_lr,
+                beta1=wl.adam_beta1, beta2=wl.adam_beta2, eps=wl.adam_eps,
+                wd=wl.adam_weight_decay, label="tiny")
+
+
+RAGGED = [(1, 1), (1, 300), (300, 1), (17, 33), (33, 17), (127, 129), (129, 127),
+          (300, 1000), (1000, 300), (256, 256), (257, 513)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_ragged_shapes(dtype):
+    Ws, Gs, Ms = wlm.random_matrix_inputs(RAGGED, dtype, seed=1)
+    run_and_check(Ws, Gs, Ms, muon_hparams(), dtype, label=f"ragged {dtype}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("variant", ["ns0", "ns1", "cubic", "no_nesterov", "custom_scale",
+                                     "zero_wd"])
+def test_variants(dtype, variant):
+    shapes = [(64, 200), (200, 64), (130, 130)]
+    Ws, Gs, Ms = wlm.random_matrix_inputs(shapes, dtype, seed=2)
+    hp = muon_hparams()
+    scales = None
+    if variant == "ns0":
+        hp["ns_steps"] = 0
+    elif variant == "ns1":
+        hp["ns_steps"] = 1
+    elif variant == "cubic":
+        hp["abc"] = (1.5, -0.5, 0.0)
+        hp["ns_steps"] = 12
+    elif variant == "no_nesterov":
+        hp["nesterov"] = False
+    elif variant == "custom_scale":
+        scales = [0.7, 2.5, 1.0]
+    elif variant == "zero_wd":
+        hp["weight_decay"] = 0.0
+    run_and_check(Ws, Gs, Ms, hp, dtype, label=variant, scales=scales)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_zero_gradient_is_decay_only(dtype):
+    shapes = [(40, 70), (70, 40)]
+    Ws, _, _ = wlm.random_matrix_inputs(shapes, dtype, seed=3)
+    Gs = [torch.zeros_like(w) for w in Ws]
+    Ms = [torch.zeros_like(w) for w in Ws]
+    st = GpuStep(Ws, Gs, Ms)
+    hp = muon_hparams()
+    st.run(**hp)
+    # the library forms 1 - lr*wd in fp32 from fp32 arguments
+    decay = np.float32(1.0) - np.float32(hp["lr"]) * np.float32(hp["weight_decay"])
+    for i, w in enumerate(Ws):
+        assert not st.U[i].any().item()
+        assert not st.M[i].any().item()
+        want = (w.to(torch.float32) * torch.tensor(decay)).to(dtype)
+        assert torch.equal(st.W[i].cpu(), want)
+
+
+# ---------------------------------------------------------------------------
+# The d=2048 block: every matrix against the oracle
+# ---------------------------------------------------------------------------
+
+def test_block_d2048_full_workload():
+    inp = wlm.generate("block_d2048", seed=0)
+    wl = inp.workload
+    run_and_check(inp.weights, inp.grads, inp.momenta, muon_hparams(wl), torch.bfloat16,
+                  label="block_d2048")
+    adamw_check(inp.tail_p, inp.tail_g, inp.tail_m, inp.tail_v, wl.adam_step,
+                lr=wl.adam_lr, beta1=wl.adam_beta1, beta2=wl.adam_beta2, eps=wl.adam_eps,
+                wd=wl.adam_weight_decay, label="block_d2048")
+
+
+# ---------------------------------------------------------------------------
+# List semantics: determinism, grouping and order independence, resume
+# ---------------------------------------------------------------------------
+
+def _subset_inputs():
+    shapes = [(512, 512), (1536, 512), (512, 1536), (300, 700), (2048, 2048)]
+    return wlm.random_matrix_inputs(shapes, torch.bfloat16, seed=4)
+
+
+def test_bitwise_determinism_and_grouping():
+    Ws, Gs, Ms = _subset_inputs()
+    hp = muon_hparams()
+    a = GpuStep(Ws, Gs, Ms)
+    a.run(**hp)
+    b = GpuStep(Ws, Gs, Ms)
+    b.run(**hp)
+    for i in range(len(Ws)):
+        assert torch.equal(a.W[i], b.W[i]) and torch.equal(a.M[i], b.M[i])
+        assert torch.equal(a.U[i], b.U[i])
+    # one matrix per call
+    for i in range(len(Ws)):
+        s = GpuStep([Ws[i]], [Gs[i]], [Ms[i]])
+        s.run(**hp)
+        assert torch.equal(s.W[0], a.W[i]) and torch.equal(s.U[0], a.U[i]), i
+    # reversed list
+    r = GpuStep(Ws[::-1], Gs[::-1], Ms[::-1])
+    r.run(**hp)
+    for i in range(len(Ws)):
+        j = len(Ws) - 1 - i
+        assert torch.equal(r.W[j], a.W[i]) and torch.equal(r.U[j], a.U[i]), i
+
+
+def test_resume_equals_continuous():
+    Ws, Gs, Ms = _subset_inputs()
+    hp = muon_hparams()
+    cont = GpuStep(Ws, Gs, Ms)
+    cont.run(**hp)
+    cont.run(**hp)
+    first = GpuStep(Ws, Gs, Ms)
+    first.run(**hp)
+    saved_w = [w.cpu() for w in first.W]
+    saved_m = [m.cpu() for m in first.M]
+    del first
+    torch.cuda.empty_cache()
+    again = GpuStep(saved_w, Gs, saved_m)
+    again.run(**hp)
+    for i in range(len(Ws)):
+        assert torch.equal(again.W[i], cont.W[i]) and torch.equal(again.M[i], cont.M[i])
