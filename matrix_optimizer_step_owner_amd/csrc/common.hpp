@@ -28,6 +28,42 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
+// Global-address-space accessors.  Pointers that come from descriptors are
+// generic; casting them to address space 1 makes the compiler emit global_*
+// instructions instead of flat_* ones (flat loads also count against the LDS
+// wait counter, which would serialize global prefetch with LDS traffic).
+#define MFSDP_GLOBAL __attribute__((address_space(1)))
+
+template <class T>
+__device__ __forceinline__ T gld(const void* p) {
+  return *(const MFSDP_GLOBAL T*)(p);
+}
+
+template <class T>
+__device__ __forceinline__ void gst(void* p, const T& v) {
+  *(MFSDP_GLOBAL T*)(p) = v;
+}
+
+// HIP's uint4/float4 are class types; go through clang vector types.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <>
+__device__ __forceinline__ uint4 gld<uint4>(const void* p) {
+  const u32x4_t v = *(const MFSDP_GLOBAL u32x4_t*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <>
+__device__ __forceinline__ void gst<uint4>(void* p, const uint4& v) {
+  *(MFSDP_GLOBAL u32x4_t*)(p) = u32x4_t{v.x, v.y, v.z, v.w};
+}
+
+template <>
+__device__ __forceinline__ void gst<float4>(void* p, const float4& v) {
+  *(MFSDP_GLOBAL f32x4_t*)(p) = f32x4_t{v.x, v.y, v.z, v.w};
+}
+
 // Element traits: storage type, elements per 16-byte vector, conversions.
 struct ElemBF16 {
   using storage_t = uint16_t;

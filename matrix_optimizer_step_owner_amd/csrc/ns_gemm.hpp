@@ -100,6 +100,65 @@ __device__ __forceinline__ void upper_tile(int local, int T, int& ti, int& tj) {
   tj = r + local;
 }
 
+// Eight consecutive storage elements <-> fp32 (one bf16 16-byte vector, or
+// two fp32 ones).  `p` must be 16-byte aligned.
+template <class E>
+__device__ __forceinline__ void load8(const typename E::storage_t* p, float (&v)[8]) {
+  if constexpr (E::kVec == 8) {
+    Vec16<E>::unpack(gld<uint4>(p), v);
+  } else {
+    float a[4], b[4];
+    Vec16<E>::unpack(gld<uint4>(p), a);
+    Vec16<E>::unpack(gld<uint4>(p + 4), b);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = a[k];
+      v[k + 4] = b[k];
+    }
+  }
+}
+
+template <class E>
+__device__ __forceinline__ void store8(typename E::storage_t* p, const float (&v)[8]) {
+  if constexpr (E::kVec == 8) {
+    gst<uint4>(p, Vec16<E>::pack(v));
+  } else {
+    const float a[4] = {v[0], v[1], v[2], v[3]};
+    const float b[4] = {v[4], v[5], v[6], v[7]};
+    gst<uint4>(p, Vec16<E>::pack(a));
+    gst<uint4>(p + 4, Vec16<E>::pack(b));
+  }
+}
+
+// W <- decay*W - lr*scale*O and update_out <- O for eight consecutive stored
+// elements at `off` (row-major in the user layout), `cnt` of them valid.
+template <class E>
+__device__ __forceinline__ void apply8(const MatDesc& d, size_t off, int cnt, bool vec,
+                                       const float (&o)[8], float decay) {
+  using S = typename E::storage_t;
+  S* W = static_cast<S*>(d.W);
+  if (vec && cnt == 8) {
+    float w[8];
+    load8<E>(W + off, w);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = fmaf(-d.lr_scale, o[k], decay * w[k]);
+    store8<E>(W + off, w);
+    if (d.upd) {
+      gst<float4>(d.upd + off, make_float4(o[0], o[1], o[2], o[3]));
+      gst<float4>(d.upd + off + 4, make_float4(o[4], o[5], o[6], o[7]));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < cnt) {
+        const float w = E::to_f32(gld<S>(W + off + k));
+        gst<S>(W + off + k, E::from_f32(fmaf(-d.lr_scale, o[k], decay * w)));
+        if (d.upd) gst<float>(d.upd + off + k, o[k]);
+      }
+    }
+  }
+}
+
 template <class E, int MODE>
 __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     const MatDesc* __restrict__ descs, WorkList wl, const float* __restrict__ scales,
@@ -152,13 +211,13 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   auto load_p = [&](int k0) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      rp[q] = *reinterpret_cast<const uint4*>(pbase + static_cast<size_t>(q * 32) * ldp + k0);
+      rp[q] = gld<uint4>(pbase + static_cast<size_t>(q * 32) * ldp + k0);
   };
   auto load_q = [&](int k0) {
-    if (MODE != kModeUpdate) {
+    if constexpr (MODE != kModeUpdate) {
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        rq[q] = *reinterpret_cast<const uint4*>(qbase_nt + static_cast<size_t>(q * 32) * ldq + k0);
+        rq[q] = gld<uint4>(qbase_nt + static_cast<size_t>(q * 32) * ldq + k0);
     } else {
       // V x V element blocks: rows k0 + kb*V + r, columns col0 + jb*V.
 #pragma unroll
@@ -167,8 +226,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
         const int kb = bi & 7, jb = bi >> 3;
 #pragma unroll
         for (int r = 0; r < V; ++r)
-          rq[h * V + r] = *reinterpret_cast<const uint4*>(
-              Q + static_cast<size_t>(k0 + kb * V + r) * ldq + col0 + jb * V);
+          rq[h * V + r] = gld<uint4>(Q + static_cast<size_t>(k0 + kb * V + r) * ldq + col0 + jb * V);
       }
     }
   };
@@ -177,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     uint4* sQ = smem[buf][1];
 #pragma unroll
     for (int q = 0; q < 8; ++q) sP[(q * 32 + prow) * 8 + pswz] = rp[q];
-    if (MODE != kModeUpdate) {
+    if constexpr (MODE != kModeUpdate) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) sQ[(q * 32 + prow) * 8 + pswz] = rq[q];
     } else {
@@ -207,9 +265,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
   const int nk = K / BK;
   load_p(0);
@@ -242,76 +298,100 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     __syncthreads();
   }
 
-  // ---- epilogue -----------------------------------------------------------
+  // ---- epilogue through LDS -------------------------------------------------
   // acc[i][j][r] sits at tile row wr*128 + i*32 + (r/4)*8 + lhalf*4 + r%4,
-  // tile column wc*128 + j*32 + lrow.
+  // tile column wc*128 + j*32 + lrow.  For each i, the four waves stage their
+  // 32 x 128 slices in LDS (fp32, padded pitch), then all threads process the
+  // 64 x 256 block with 16-byte row-contiguous global accesses; a second,
+  // column-wise pass writes the mirrored tile of a symmetric product or the
+  // transposed apply of a tall matrix.
+  constexpr int SP = 132;               // staged row pitch in floats
+  constexpr int WREG = 32 * SP;         // floats per wave slice
+  float* stage = reinterpret_cast<float*>(&smem[0][0][0]);
   const float s_norm = scales[k];
-  if (MODE == kModeGram || MODE == kModePoly) {
-    S* out = static_cast<S*>(MODE == kModeGram ? d.A : d.B);
-    const S* Ain = static_cast<const S*>(d.A);
-    const int ld = d.m_pad;
-    const float alpha = (MODE == kModeGram && ep.first) ? s_norm * s_norm : 1.f;
-    const bool mirror = ti != tj;
+  const bool sym = MODE != kModeUpdate;
+  const bool mirror = sym && ti != tj;
+  const bool tall_apply = MODE == kModeUpdate && ep.last && d.tall;
+  const float alpha = MODE == kModeGram ? (ep.first ? s_norm * s_norm : 1.f)
+                    : MODE == kModeUpdate ? (ep.first ? s_norm : 1.f) : 1.f;
+  S* out = static_cast<S*>(MODE == kModeGram ? d.A : MODE == kModePoly ? d.B
+                                             : (ep.cur ? d.X0 : d.X1));
+  const int ldo = sym ? d.m_pad : d.n_pad;
+  const bool vec = d.vec_ok != 0;
+
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = col0 + wc * 128 + j * 32 + lrow;
-          const int rbase = row0 + wr * 128 + i * 32 + g * 8 + lhalf * 4;
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float x = acc[i][j][g * 4 + r];
-            if (MODE == kModeGram) {
-              v[r] = alpha * x;
-            } else {
-              const float aij = E::to_f32(Ain[static_cast<size_t>(rbase + r) * ld + col]);
-              v[r] = fmaf(ep.c, x, ep.b * aij);
-            }
-          }
-          S sv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            sv[r] = E::from_f32(v[r]);
-            out[static_cast<size_t>(rbase + r) * ld + col] = sv[r];
-          }
-          if (mirror) {
-            S* mp = out + static_cast<size_t>(col) * ld + rbase;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mp[r] = sv[r];
-          }
-        }
-  } else {
-    const float alpha = ep.first ? s_norm : 1.f;
-    S* Xnext = static_cast<S*>(ep.cur ? d.X0 : d.X1);
-    S* W = static_cast<S*>(d.W);
-    const int ld = d.n_pad;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    {
+      float* reg = stage + wave * WREG;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = col0 + wc * 128 + j * 32 + lrow;
-          const int rbase = row0 + wr * 128 + i * 32 + g * 8 + lhalf * 4;
+        for (int r = 0; r < 16; ++r)
+          reg[((r >> 2) * 8 + lhalf * 4 + (r & 3)) * SP + j * 32 + lrow] = acc[i][j][r];
+    }
+    __syncthreads();
+
+    // Pass A: row-major, eight consecutive columns per thread.
+    for (int p = 0; p < 8; ++p) {
+      const int it = p * kThreads + tid;
+      const int rr = it >> 5, cv = it & 31;
+      const int wrr = rr >> 5, r_in = rr & 31, wcc = cv >> 4, c_in = (cv & 15) * 8;
+      float* src = stage + (wrr * 2 + wcc) * WREG + r_in * SP + c_in;
+      const float4 lo = *reinterpret_cast<const float4*>(src);
+      const float4 hi = *reinterpret_cast<const float4*>(src + 4);
+      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const int grow = row0 + wrr * 128 + i * 32 + r_in;
+      const int gcol = col0 + wcc * 128 + c_in;
+      const size_t goff = static_cast<size_t>(grow) * ldo + gcol;
+      if (MODE == kModeGram) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = rbase + r;
-            const size_t off = static_cast<size_t>(row) * ld + col;
-            const float x = E::to_f32(Xcur[off]);
-            const float v = alpha * fmaf(ep.kb, acc[i][j][g * 4 + r], ep.a * x);
-            if (!ep.last) {
-              Xnext[off] = E::from_f32(v);
-            } else if (row < d.m && col < d.n) {
-              const size_t uo = d.tall ? static_cast<size_t>(col) * d.cols + row
-                                       : static_cast<size_t>(row) * d.cols + col;
-              W[uo] = E::from_f32(fmaf(-d.lr_scale, v, ep.decay * E::to_f32(W[uo])));
-              if (d.upd) d.upd[uo] = v;
-            }
-          }
+        for (int e = 0; e < 8; ++e) v[e] *= alpha;
+      } else if (MODE == kModePoly) {
+        float a8[8];
+        load8<E>(static_cast<const S*>(d.A) + goff, a8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = fmaf(ep.c, v[e], ep.b * a8[e]);
+      } else {
+        float x8[8];
+        load8<E>(Xcur + goff, x8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = alpha * fmaf(ep.kb, v[e], ep.a * x8[e]);
+      }
+      if (MODE != kModeUpdate || !ep.last) {
+        store8<E>(out + goff, v);
+      } else if (!d.tall) {
+        if (grow < d.m && gcol < d.n)
+          apply8<E>(d, static_cast<size_t>(grow) * d.cols + gcol, min(8, d.n - gcol), vec, v,
+                    ep.decay);
+      }
+      if (mirror || tall_apply) {
+        *reinterpret_cast<float4*>(src) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(src + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+
+    // Pass B: column-wise, eight consecutive tile rows of one tile column.
+    if (mirror || tall_apply) {
+      __syncthreads();
+      for (int p = 0; p < 8; ++p) {
+        const int it = p * kThreads + tid;
+        const int tc = it >> 3, q = it & 7;
+        const int wrr = q >> 2, sub = q & 3, wcc = tc >> 7, c_in = tc & 127;
+        const float* src = stage + (wrr * 2 + wcc) * WREG + (sub * 8) * SP + c_in;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = src[e * SP];
+        const int grow0 = row0 + wrr * 128 + i * 32 + sub * 8;
+        const int gcol = col0 + tc;
+        if (mirror) {
+          store8<E>(out + static_cast<size_t>(gcol) * ldo + grow0, v);
+        } else if (gcol < d.n && grow0 < d.m) {
+          apply8<E>(d, static_cast<size_t>(gcol) * d.cols + grow0, min(8, d.m - grow0), vec, v,
+                    ep.decay);
         }
+      }
+    }
+    __syncthreads();
   }
 }
 
