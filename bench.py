@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--workload", default="block_d2048")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before the run, copy this many MiB device-to-device with a plain "
+                         "copy kernel (reference point for HBM byte counters)")
     ap.add_argument("--traffic", default=None,
                     help="JSON file with measured HBM bytes per launch of the dominant kernel")
     args = ap.parse_args()
@@ -118,6 +121,13 @@ def main():
     from matrix_optimizer_step_owner_amd import workloads as wlm
 
     dev = torch.device("cuda:0")
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = wlm.WORKLOADS[args.workload]
     inp = wlm.generate(args.workload, seed=0)
     shapes = [(s.rows, s.cols) for s in wl.matrices]

@@ -16,12 +16,18 @@ constexpr int kThreads = 256;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32, which also
+// keeps NaN a NaN).  Two values per instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.f) & 0xffffu);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -33,6 +39,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 // instructions instead of flat_* ones (flat loads also count against the LDS
 // wait counter, which would serialize global prefetch with LDS traffic).
 #define MFSDP_GLOBAL __attribute__((address_space(1)))
+#define MFSDP_LDS __attribute__((address_space(3)))
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
 
 template <class T>
 __device__ __forceinline__ T gld(const void* p) {
@@ -101,12 +111,8 @@ struct Vec16<ElemBF16> {
     }
   }
   __device__ __forceinline__ static uint4 pack(const float (&in)[8]) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(f32_to_bf16_rne(in[2 * i])) |
-             (static_cast<uint32_t>(f32_to_bf16_rne(in[2 * i + 1])) << 16);
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    return make_uint4(pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3]),
+                      pack_bf16x2(in[4], in[5]), pack_bf16x2(in[6], in[7]));
   }
 };
 
@@ -162,6 +168,19 @@ __device__ __forceinline__ int find_item(const WorkList& wl, int32_t bid) {
     if (wl.begin[mid] <= bid) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8), and each XCD has its own L2.  Remap so that XCD x processes a
+// contiguous range of logical tiles, in order: neighbouring tiles (which share
+// operand panels) then run on the same XCD and hit in its L2.  A bijection on
+// [0, nblocks).
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_remap(int b, int nblocks) {
+  const int x = b % kXcds, i = b / kXcds;
+  const int q = nblocks / kXcds, r = nblocks % kXcds;
+  return x * q + (x < r ? x : r) + i;
 }
 
 __device__ __forceinline__ float warp_sum(float v) {

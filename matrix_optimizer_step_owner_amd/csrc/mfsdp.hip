@@ -123,7 +123,7 @@ struct MatGeom {
 
 struct Plan {
   std::vector<MatGeom> geom;
-  size_t off_descs = 0, off_lists = 0, off_scales = 0, off_partials = 0;
+  size_t off_descs = 0, off_lists = 0, off_tiles = 0, off_scales = 0, off_partials = 0;
   size_t blob_bytes = 0;            // descriptors + work lists (host upload)
   std::vector<size_t> off_x0, off_x1, off_a, off_b;
   size_t total = 0;
@@ -169,6 +169,9 @@ mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t d
   p->off_lists = off;
   // three work lists (momentum, symmetric products, update): mat[n], begin[n+1]
   off = align_up(off + 3 * (2 * n + 1) * sizeof(int32_t), kWsAlign);
+  // per-tile (matrix, tile) tables of the symmetric and update launches
+  p->off_tiles = off;
+  off = align_up(off + (p->gram_total + p->upd_total) * sizeof(int2), kWsAlign);
   p->blob_bytes = off;
   p->off_scales = off;
   off = align_up(off + n * sizeof(float), kWsAlign);
@@ -241,7 +244,9 @@ hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nest
     wl.n_items = static_cast<int32_t>(n);
     return wl;
   };
-  const WorkList wl_ew = list(0), wl_sym = list(1), wl_upd = list(2);
+  const WorkList wl_ew = list(0);
+  const int2* tiles_sym = reinterpret_cast<const int2*>(ws + p.off_tiles);
+  const int2* tiles_upd = tiles_sym + p.gram_total;
   float* scales = reinterpret_cast<float*>(ws + p.off_scales);
   double* partials = reinterpret_cast<double*>(ws + p.off_partials);
 
@@ -268,7 +273,6 @@ hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nest
     NsEpi ep;
     ep.cur = it & 1;
     ep.first = it == 0;
-    ep.last = it == ns_steps - 1;
     ep.b_is_A = skip_poly ? 1 : 0;
     ep.a = a;
     ep.b = b;
@@ -277,19 +281,24 @@ hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nest
     ep.decay = decay;
     e = launch(MFSDP_KERNEL_GRAM, stream, [&] {
       ns_gemm_kernel<E, kModeGram><<<dim3(static_cast<unsigned>(p.gram_total)), dim3(kThreads), 0,
-                                     stream>>>(descs, wl_sym, scales, ep);
+                                     stream>>>(descs, tiles_sym, scales, ep);
     });
     if (e != hipSuccess) return e;
     if (!skip_poly) {
       e = launch(MFSDP_KERNEL_POLY, stream, [&] {
         ns_gemm_kernel<E, kModePoly><<<dim3(static_cast<unsigned>(p.gram_total)), dim3(kThreads), 0,
-                                       stream>>>(descs, wl_sym, scales, ep);
+                                       stream>>>(descs, tiles_sym, scales, ep);
       });
       if (e != hipSuccess) return e;
     }
+    const bool last = it == ns_steps - 1;
     e = launch(MFSDP_KERNEL_UPDATE, stream, [&] {
-      ns_gemm_kernel<E, kModeUpdate><<<dim3(static_cast<unsigned>(p.upd_total)), dim3(kThreads), 0,
-                                       stream>>>(descs, wl_upd, scales, ep);
+      if (last)
+        ns_gemm_kernel<E, kModeApply><<<dim3(static_cast<unsigned>(p.upd_total)), dim3(kThreads),
+                                        0, stream>>>(descs, tiles_upd, scales, ep);
+      else
+        ns_gemm_kernel<E, kModeUpdate><<<dim3(static_cast<unsigned>(p.upd_total)), dim3(kThreads),
+                                         0, stream>>>(descs, tiles_upd, scales, ep);
     });
     if (e != hipSuccess) return e;
   }
@@ -448,6 +457,16 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
   }
   fill_list(lists + (2 * n_mats + 1), lists + (2 * n_mats + 1) + n_mats, t_sym, k_gram);
   fill_list(lists + 2 * (2 * n_mats + 1), lists + 2 * (2 * n_mats + 1) + n_mats, t_upd, k_upd);
+  {
+    // expand the two GEMM work lists into per-tile tables
+    int2* tab = reinterpret_cast<int2*>(blob.data() + p.off_tiles);
+    for (int which = 1; which <= 2; ++which) {
+      const int32_t* mat = lists + which * (2 * n_mats + 1);
+      const int32_t* begin = mat + n_mats;
+      for (int64_t it = 0; it < n_mats; ++it)
+        for (int32_t t = 0; t < begin[it + 1] - begin[it]; ++t) *tab++ = make_int2(mat[it], t);
+    }
+  }
 
   hipError_t e = hipMemcpyAsync(ws, blob.data(), p.blob_bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "descriptor upload: %s", hipGetErrorString(e));

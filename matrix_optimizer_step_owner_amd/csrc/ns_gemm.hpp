@@ -10,23 +10,29 @@
 // alpha = s, where s = 1 / (||U||_F + eps).
 //
 // Kernel shape: 256 threads (4 waves) per 256x256 output tile, each wave a
-// 128x128 quadrant of 4x4 MFMA 32x32 blocks.  The K loop stages 256 x 128-byte
-// panels of both operands in LDS (double buffered, 128 KB), rows XOR-swizzled
-// in 16-byte chunks so the fragment reads are bank-conflict free.  The
-// K-strided operand of the update (X, read by columns) is transposed in
-// registers on its way into LDS, so both LDS panels are K-contiguous.
+// 128x128 quadrant of 4x4 MFMA 32x32 blocks.  Operand panels (one K step: 64
+// bf16 or 32 fp32 per row) go from global memory straight into LDS
+// (global_load_lds_dwordx4, no register staging), double buffered (128 KB);
+// rows are XOR-swizzled in 16-byte chunks so fragment reads are free of bank
+// conflicts.  The update's K-strided operand X keeps its row-major layout in
+// LDS and is read with the gfx950 transposing LDS load (ds_read_b64_tr_b16),
+// which hands each lane four consecutive K values of its own column.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
 namespace mfsdp {
 
-enum NsMode { kModeGram = 0, kModePoly = 1, kModeUpdate = 2 };
+// kModeUpdate writes the next iterate; kModeApply is the update of the last
+// iteration, which applies W (and update_out) instead.  Separate kernels keep
+// the apply code out of the update that runs on every other iteration.
+enum NsMode { kModeGram = 0, kModePoly = 1, kModeUpdate = 2, kModeApply = 3 };
 
 struct NsEpi {
   int cur;        // 0: the current iterate is X0, 1: X1
   int first;      // first iteration (apply the normalization factor)
-  int last;       // last iteration (apply W and update_out)
   int b_is_A;     // c == 0: the update multiplies A (scaled by kb = b)
   float a, b, c;
   float kb;       // factor of the B X product in the update epilogue
@@ -53,40 +59,6 @@ struct Mma<ElemF32> {
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
-  }
-};
-
-// 16-byte element `cc` extraction helpers for the register transpose.
-template <class E>
-struct Transpose;
-
-template <>
-struct Transpose<ElemBF16> {
-  // in[r] holds row r (8 bf16 along j); out[c] gets column c (8 bf16 along k).
-  __device__ __forceinline__ static void run(const uint4 (&in)[8], uint4 (&out)[8]) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t w[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint4& r0 = in[2 * d];
-        const uint4& r1 = in[2 * d + 1];
-        const uint32_t s0 = (c >> 1) == 0 ? r0.x : (c >> 1) == 1 ? r0.y : (c >> 1) == 2 ? r0.z : r0.w;
-        const uint32_t s1 = (c >> 1) == 0 ? r1.x : (c >> 1) == 1 ? r1.y : (c >> 1) == 2 ? r1.z : r1.w;
-        w[d] = (c & 1) ? ((s0 >> 16) | (s1 & 0xffff0000u)) : ((s0 & 0xffffu) | (s1 << 16));
-      }
-      out[c] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
-};
-
-template <>
-struct Transpose<ElemF32> {
-  __device__ __forceinline__ static void run(const uint4 (&in)[4], uint4 (&out)[4]) {
-    out[0] = make_uint4(in[0].x, in[1].x, in[2].x, in[3].x);
-    out[1] = make_uint4(in[0].y, in[1].y, in[2].y, in[3].y);
-    out[2] = make_uint4(in[0].z, in[1].z, in[2].z, in[3].z);
-    out[3] = make_uint4(in[0].w, in[1].w, in[2].w, in[3].w);
   }
 };
 
@@ -130,55 +102,132 @@ __device__ __forceinline__ void store8(typename E::storage_t* p, const float (&v
   }
 }
 
-// W <- decay*W - lr*scale*O and update_out <- O for eight consecutive stored
-// elements at `off` (row-major in the user layout), `cnt` of them valid.
+// Eight consecutive storage elements as raw 16-byte words (bf16: a only).
+struct Raw8 {
+  uint4 a, b;
+};
+
 template <class E>
-__device__ __forceinline__ void apply8(const MatDesc& d, size_t off, int cnt, bool vec,
-                                       const float (&o)[8], float decay) {
-  using S = typename E::storage_t;
-  S* W = static_cast<S*>(d.W);
-  if (vec && cnt == 8) {
-    float w[8];
-    load8<E>(W + off, w);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) w[k] = fmaf(-d.lr_scale, o[k], decay * w[k]);
-    store8<E>(W + off, w);
-    if (d.upd) {
-      gst<float4>(d.upd + off, make_float4(o[0], o[1], o[2], o[3]));
-      gst<float4>(d.upd + off + 4, make_float4(o[4], o[5], o[6], o[7]));
-    }
+__device__ __forceinline__ Raw8 load_raw8(const typename E::storage_t* p) {
+  Raw8 r;
+  r.a = gld<uint4>(p);
+  if constexpr (E::kVec == 4)
+    r.b = gld<uint4>(p + 4);
+  else
+    r.b = make_uint4(0, 0, 0, 0);
+  return r;
+}
+
+template <class E>
+__device__ __forceinline__ void unpack_raw8(const Raw8& r, float (&v)[8]) {
+  if constexpr (E::kVec == 8) {
+    Vec16<E>::unpack(r.a, v);
   } else {
+    float a[4], b[4];
+    Vec16<E>::unpack(r.a, a);
+    Vec16<E>::unpack(r.b, b);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (k < cnt) {
-        const float w = E::to_f32(gld<S>(W + off + k));
-        gst<S>(W + off + k, E::from_f32(fmaf(-d.lr_scale, o[k], decay * w)));
-        if (d.upd) gst<float>(d.upd + off + k, o[k]);
-      }
+    for (int k = 0; k < 4; ++k) {
+      v[k] = a[k];
+      v[k + 4] = b[k];
     }
   }
 }
 
+// W <- decay*W - lr*scale*O and update_out <- O for eight consecutive stored
+// elements at `off` (row-major in the user layout); `w` holds their current
+// values (loaded beforehand).
+template <class E>
+__device__ __forceinline__ void apply8_vec(const MatDesc& d, size_t off, const Raw8& w,
+                                           const float (&o)[8], float decay) {
+  using S = typename E::storage_t;
+  float wv[8];
+  unpack_raw8<E>(w, wv);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) wv[k] = fmaf(-d.lr_scale, o[k], decay * wv[k]);
+  store8<E>(static_cast<S*>(d.W) + off, wv);
+  if (d.upd) {
+    gst<float4>(d.upd + off, make_float4(o[0], o[1], o[2], o[3]));
+    gst<float4>(d.upd + off + 4, make_float4(o[4], o[5], o[6], o[7]));
+  }
+}
+
+// Same for `cnt` (< 8 or unaligned) elements, one at a time.
+template <class E>
+__device__ __noinline__ void apply8_scalar(const MatDesc& d, size_t off, int cnt,
+                                              const float (&o)[8], float decay) {
+  using S = typename E::storage_t;
+  S* W = static_cast<S*>(d.W);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k < cnt) {
+      const float w = E::to_f32(gld<S>(W + off + k));
+      gst<S>(W + off + k, E::from_f32(fmaf(-d.lr_scale, o[k], decay * w)));
+      if (d.upd) gst<float>(d.upd + off + k, o[k]);
+    }
+  }
+}
+
+// One wave-wide global -> LDS copy of 64 x 16 bytes (global_load_lds_dwordx4):
+// lane l reads 16 bytes at sbase + voff and writes them to LDS at
+// lds + 16*l.  Issued as inline assembly so that the compiler does not track
+// it: its wait-count pass cannot tell the pipeline stages apart and would
+// wait for every DMA in flight before each LDS read.  The kernel waits for
+// these copies itself (vmcnt) before the block barriers that publish them.
+// M0 holds the LDS base; nothing else in these kernels uses M0.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, const void* sbase) {
+  // The base is wave-uniform; make that explicit so it lives in SGPRs.
+  // readfirstlane returns a signed int: widen through uint32_t, never
+  // directly (a sign extension would corrupt the high word of any address
+  // whose bit 31 is set).
+  const uint64_t b = reinterpret_cast<uintptr_t>(sbase);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  const uint32_t hi =
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const uint64_t ub = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(ub) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((MFSDP_LDS const void*)p)));
+}
+
+// XOR swizzle of the 16-byte chunks of a K-contiguous LDS panel row (64 bytes).
+// The LDS serves 16 lanes x 16 bytes per cycle from 64 banks, i.e. four panel
+// rows per bank row; a fragment read touches 16 consecutive rows at one
+// chunk, which (row >> 2) & 3 spreads over all 16 bank groups.
+__device__ __forceinline__ int kswz(int row) { return (row >> 2) & 3; }
+
 template <class E, int MODE>
 __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
-    const MatDesc* __restrict__ descs, WorkList wl, const float* __restrict__ scales,
-    NsEpi ep) {
+    const MatDesc* __restrict__ descs, const int2* __restrict__ tiles,
+    const float* __restrict__ scales, NsEpi ep) {
   using S = typename E::storage_t;
   constexpr int V = E::kVec;            // elements per 16-byte chunk
-  constexpr int BK = 8 * V;             // K elements per 128-byte panel row
-  constexpr int PANEL = kTile * 8;      // uint4 per operand panel
+  constexpr int BK = 4 * V;             // K elements per 64-byte panel row
+  constexpr int PANEL = kTile * 4;      // uint4 per operand panel (16 KB)
+  constexpr int kStages = 4;            // LDS pipeline depth (4 x 32 KB)
 
-  __shared__ uint4 smem[2][2][PANEL];   // [buffer][operand P/Q][row*8+chunk]
+  // Pipeline stages, each holding the P panel then the Q panel.  Separate
+  // objects so that the compiler can tell a DMA into one stage from reads of
+  // another and does not serialize them.
+  __shared__ uint4 st0[2 * PANEL];
+  __shared__ uint4 st1[2 * PANEL];
+  __shared__ uint4 st2[2 * PANEL];
+  __shared__ uint4 st3[2 * PANEL];
 
   const int tid = threadIdx.x;
-  const int bid = blockIdx.x;
-  const int item = find_item(wl, bid);
-  const int k = wl.mat[item];
+  // tiles[b] = (matrix, tile index within it) of logical tile b
+  const int2 tile = tiles[xcd_remap(blockIdx.x, gridDim.x)];
+  const int k = tile.x;
+  const int local = tile.y;
   const MatDesc d = descs[k];
-  const int local = bid - wl.begin[item];
 
+  constexpr bool kUpd = MODE == kModeUpdate || MODE == kModeApply;
   int ti, tj;
-  if (MODE == kModeUpdate) {
+  if (kUpd) {
     const int tn = d.n_pad / kTile;
     ti = local / tn;
     tj = local % tn;
@@ -200,66 +249,101 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     Q = Xcur; ldq = d.n_pad; K = d.m_pad;
   }
 
-  // ---- global -> register staging -------------------------------------
-  // Operand P (and Q for gram/poly): rows of the output tile, K-contiguous.
-  const int prow = tid >> 3, pchunk = tid & 7;
-  const int pswz = pchunk ^ (prow & 7);
-  const S* pbase = P + static_cast<size_t>(row0 + prow) * ldp + pchunk * V;
-  const S* qbase_nt = Q + static_cast<size_t>(col0 + prow) * ldq + pchunk * V;
-  uint4 rp[8], rq[8];
-
-  auto load_p = [&](int k0) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      rp[q] = gld<uint4>(pbase + static_cast<size_t>(q * 32) * ldp + k0);
-  };
-  auto load_q = [&](int k0) {
-    if constexpr (MODE != kModeUpdate) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        rq[q] = gld<uint4>(qbase_nt + static_cast<size_t>(q * 32) * ldq + k0);
-    } else {
-      // V x V element blocks: rows k0 + kb*V + r, columns col0 + jb*V.
-#pragma unroll
-      for (int h = 0; h < 8 / V; ++h) {
-        const int bi = tid + h * kThreads;
-        const int kb = bi & 7, jb = bi >> 3;
-#pragma unroll
-        for (int r = 0; r < V; ++r)
-          rq[h * V + r] = gld<uint4>(Q + static_cast<size_t>(k0 + kb * V + r) * ldq + col0 + jb * V);
-      }
-    }
-  };
-  auto store_lds = [&](int buf) {
-    uint4* sP = smem[buf][0];
-    uint4* sQ = smem[buf][1];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) sP[(q * 32 + prow) * 8 + pswz] = rp[q];
-    if constexpr (MODE != kModeUpdate) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) sQ[(q * 32 + prow) * 8 + pswz] = rq[q];
-    } else {
-#pragma unroll
-      for (int h = 0; h < 8 / V; ++h) {
-        const int bi = tid + h * kThreads;
-        const int kb = bi & 7, jb = bi >> 3;
-        uint4 in[V], out[V];
-#pragma unroll
-        for (int r = 0; r < V; ++r) in[r] = rq[h * V + r];
-        Transpose<E>::run(in, out);
-#pragma unroll
-        for (int c = 0; c < V; ++c) {
-          const int j = jb * V + c;
-          sQ[j * 8 + (kb ^ (j & 7))] = out[c];
-        }
-      }
-    }
-  };
-
-  // ---- MFMA main loop -----------------------------------------------------
-  const int lane = tid & 63, wave = tid >> 6;
+  // ---- operand panels: global -> LDS by DMA ---------------------------------
+  // Each wave issues global_load_lds_dwordx4: lane l's 16 bytes land at
+  // LDS base + 16*l, so the lane picks the global chunk that belongs at that
+  // swizzled position.  K-contiguous panels: 256 rows x 4 chunks of 16 bytes,
+  // chunk c of row r stored at r*4 + (c ^ kswz(r)).  The K-strided panel of
+  // the update (X, bf16): 32 k-rows x 32 chunks (256 columns), chunk c of row k
+  // at k*32 + (c ^ 4*(k & 3)); fp32: 16 k-rows x 64 chunks, unswizzled.
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
   const int lrow = lane & 31, lhalf = lane >> 5;
+
+  // DMA piece q (0..7) of one K step: pieces 0..3 fill the P panel, 4..7 the
+  // Q panel; each piece is one 1 KB wave instruction.  The per-lane byte
+  // offset of a piece is fixed for the whole K loop; only the uniform base
+  // moves with k0 (SGPR base + constant VGPR offset, no address VALU).
+  uint32_t doff[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int u = wave * 256 + (q & 3) * 64 + lane;
+    if (q < 4 || !kUpd) {
+      const int ld = q < 4 ? ldp : ldq;
+      const int r0 = q < 4 ? row0 : col0;
+      const int row = u >> 2, c = (u & 3) ^ kswz(row);
+      doff[q] = static_cast<uint32_t>((static_cast<size_t>(r0 + row) * ld + c * V) * sizeof(S));
+    } else {
+      constexpr int UPR = kTile / V;    // 16-byte chunks per k-row
+      const int kk = u / UPR, pc = u % UPR;
+      const int c = (V == 8) ? (pc ^ (4 * (kk & 3))) : pc;
+      doff[q] = static_cast<uint32_t>((static_cast<size_t>(kk) * ldq + col0 + c * V) * sizeof(S));
+    }
+  }
+  auto dma_piece = [&](uint4* buf, int k0, int q) {
+    const char* base;
+    if (q < 4)
+      base = reinterpret_cast<const char*>(P + k0);
+    else if (!kUpd)
+      base = reinterpret_cast<const char*>(Q + k0);
+    else
+      base = reinterpret_cast<const char*>(Q + static_cast<size_t>(k0) * ldq);
+    uint4* dst = buf + (q < 4 ? 0 : PANEL) + wave * 256 + (q & 3) * 64;
+    lds_dma16(lds_addr(dst), doff[q], base);
+  };
+
+  // ---- fragments --------------------------------------------------------------
+  // Lane l holds, for K sub-step s (0, 1), the 16-byte K-slice 2s + l/32
+  // (bf16: K = 8*(2s + l/32) .. +8) of output row l%32 of each 32-row block.
+  // Read piece p: 0..3 the P fragments fa[i]; then the Q fragments (NT: one
+  // piece per fb[j]; bf16 update: two transposing reads per fb[j]).
+  constexpr int kReadPieces = (kUpd && V == 8) ? 12 : 8;
+  auto read_piece = [&](const uint4* buf, int s, int p, uint4 (&fa)[4], uint4 (&fb)[4]) {
+    const int c = 2 * s + lhalf;
+    if (p < 4) {
+      const int row = wr * 128 + p * 32 + lrow;
+      fa[p] = buf[row * 4 + (c ^ kswz(row))];
+      return;
+    }
+    const uint4* qp = buf + PANEL;
+    if constexpr (!kUpd) {
+      const int j = p - 4;
+      const int row = wc * 128 + j * 32 + lrow;
+      fb[j] = qp[row * 4 + (c ^ kswz(row))];
+    } else if constexpr (V == 8) {
+      // Transposing read: within each 16-lane group, lane i points at k-row
+      // kb + i/4, columns n0 + 4*(i%4) .. +4; lane j receives column n0 + j
+      // at k-rows kb .. kb+3.
+      const int j = (p - 4) >> 1, r = (p - 4) & 1;
+      const int il = lane & 15;
+      const int n = wc * 128 + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (il & 3);
+      const int kk = 16 * s + 8 * lhalf + 4 * r + (il >> 2);
+      const int byte = kk * 512 + (((n >> 3) ^ (4 * (kk & 3))) << 4) + ((n & 7) << 1);
+      const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (MFSDP_LDS v4i16_t*)(reinterpret_cast<const char*>(qp) + byte));
+      const uint32_t w0 = static_cast<uint16_t>(t[0]) |
+                          (static_cast<uint32_t>(static_cast<uint16_t>(t[1])) << 16);
+      const uint32_t w1 = static_cast<uint16_t>(t[2]) |
+                          (static_cast<uint32_t>(static_cast<uint16_t>(t[3])) << 16);
+      if (r == 0) {
+        fb[j].x = w0;
+        fb[j].y = w1;
+      } else {
+        fb[j].z = w0;
+        fb[j].w = w1;
+      }
+    } else {
+      const int j = p - 4;
+      const float* qf = reinterpret_cast<const float*>(qp);
+      const int n = wc * 128 + j * 32 + lrow;
+      const int kk = 4 * c;
+      fb[j] = make_uint4(__float_as_uint(qf[(kk + 0) * kTile + n]),
+                         __float_as_uint(qf[(kk + 1) * kTile + n]),
+                         __float_as_uint(qf[(kk + 2) * kTile + n]),
+                         __float_as_uint(qf[(kk + 3) * kTile + n]));
+    }
+  };
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -267,132 +351,230 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-  const int nk = K / BK;
-  load_p(0);
-  load_q(0);
-  store_lds(0);
-  __syncthreads();
+  uint4 fa[2][4], fb[2][4];
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      load_p((kt + 1) * BK);
-      load_q((kt + 1) * BK);
+  // One K step t on stage buffer X.  Sub-step 0 issues its 16 MFMAs one per
+  // slot; each slot also issues one fragment read of sub-step 1 and (when
+  // DMA) one DMA piece of step t + kStages - 1 into stage Y, the buffer of
+  // step t - 1.  Then: wait until the DMA of step t + 1 has landed (the two
+  // most recent steps' DMAs may stay in flight), block barrier.  Sub-step 1's
+  // MFMAs overlap the fragment reads of step t + 1 from stage N.
+  // The barrier also orders every wave's last reads of stage Y (issued before
+  // the previous barrier) before the DMA into Y.
+  auto kstep = [&](const uint4* X, uint4* Y, const uint4* N, int k_dma, auto dma_c,
+                   auto next_c, auto wait_all_c) {
+    constexpr bool do_dma = decltype(dma_c)::value;
+    constexpr bool has_next = decltype(next_c)::value;
+    constexpr bool wait_all = decltype(wait_all_c)::value;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      Mma<E>::run(acc[idx >> 2][idx & 3], fa[0][idx >> 2], fb[0][idx & 3]);
+      if (idx < kReadPieces) read_piece(X, 1, idx, fa[1], fb[1]);
+      if constexpr (do_dma) {
+        if (idx < 8) dma_piece(Y, k_dma, idx);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const uint4* sP = smem[cur][0];
-    const uint4* sQ = smem[cur][1];
+    // Block barrier without the release fence of __syncthreads(), which would
+    // also wait for the DMAs still in flight; the memory clobber keeps the
+    // compiler from moving LDS accesses across it.
+    if constexpr (wait_all)
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int ch = (2 * s + lhalf) ^ (lrow & 7);
-      uint4 fa[4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = sP[(wr * 128 + i * 32 + lrow) * 8 + ch];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = sQ[(wc * 128 + j * 32 + lrow) * 8 + ch];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Mma<E>::run(acc[i][j], fa[i], fb[j]);
+    for (int idx = 0; idx < 16; ++idx) {
+      Mma<E>::run(acc[idx >> 2][idx & 3], fa[1][idx >> 2], fb[1][idx & 3]);
+      if constexpr (has_next) {
+        if (idx < kReadPieces) read_piece(N, 0, idx, fa[0], fb[0]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
-    __syncthreads();
+  };
+
+  // ---- main loop: four stages, unrolled by four ----------------------------
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  const int nk = K / BK;                // multiple of 8: K is a multiple of 256
+  // prologue: steps 0..2 in flight, wait for step 0
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_piece(st0, 0, q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_piece(st1, BK, q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_piece(st2, 2 * BK, q);
+  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int p = 0; p < kReadPieces; ++p) read_piece(st0, 0, p, fa[0], fb[0]);
+  int t = 0;
+  for (; t + 8 <= nk; t += 4) {
+    kstep(st0, st3, st1, (t + 3) * BK, yes{}, yes{}, no{});
+    kstep(st1, st0, st2, (t + 4) * BK, yes{}, yes{}, no{});
+    kstep(st2, st1, st3, (t + 5) * BK, yes{}, yes{}, no{});
+    kstep(st3, st2, st0, (t + 6) * BK, yes{}, yes{}, no{});
   }
+  // last four steps: only the first still has a step (nk - 1) to prefetch
+  kstep(st0, st3, st1, (t + 3) * BK, yes{}, yes{}, yes{});
+  kstep(st1, st0, st2, 0, no{}, yes{}, yes{});
+  kstep(st2, st1, st3, 0, no{}, yes{}, yes{});
+  kstep(st3, st2, st0, 0, no{}, no{}, yes{});
+  __syncthreads();
 
   // ---- epilogue through LDS -------------------------------------------------
   // acc[i][j][r] sits at tile row wr*128 + i*32 + (r/4)*8 + lhalf*4 + r%4,
   // tile column wc*128 + j*32 + lrow.  For each i, the four waves stage their
-  // 32 x 128 slices in LDS (fp32, padded pitch), then all threads process the
-  // 64 x 256 block with 16-byte row-contiguous global accesses; a second,
+  // 32 x 128 slices in LDS (fp32), then all threads process the 64 x 256 block
+  // with 16-byte row-contiguous global accesses (pass A); a second,
   // column-wise pass writes the mirrored tile of a symmetric product or the
-  // transposed apply of a tall matrix.
-  constexpr int SP = 132;               // staged row pitch in floats
-  constexpr int WREG = 32 * SP;         // floats per wave slice
-  float* stage = reinterpret_cast<float*>(&smem[0][0][0]);
+  // transposed apply of a tall matrix (pass B).  Every global input of a pass
+  // is loaded before its first store: the stores may alias the inputs as far
+  // as the compiler knows, so interleaving them would serialize on latency.
+  constexpr int SP = 128;               // staged row pitch in floats
+  // column c of staged row r lives at r*SP + (c ^ 4*((r >> 2) & 7))
+  auto sidx = [](int r, int c) { return r * SP + (c ^ (((r >> 2) & 7) << 2)); };
+  // wave slice w lives in stage array w (16 KB of its 32 KB)
+  auto slice_of = [&](int w) -> float* {
+    return reinterpret_cast<float*>(w == 0 ? st0 : w == 1 ? st1 : w == 2 ? st2 : st3);
+  };
   const float s_norm = scales[k];
-  const bool sym = MODE != kModeUpdate;
+  constexpr bool sym = !kUpd;
   const bool mirror = sym && ti != tj;
-  const bool tall_apply = MODE == kModeUpdate && ep.last && d.tall;
+  const bool wide_apply = MODE == kModeApply && !d.tall;
+  const bool tall_apply = MODE == kModeApply && d.tall;
   const float alpha = MODE == kModeGram ? (ep.first ? s_norm * s_norm : 1.f)
-                    : MODE == kModeUpdate ? (ep.first ? s_norm : 1.f) : 1.f;
+                    : kUpd ? (ep.first ? s_norm : 1.f) : 1.f;
   S* out = static_cast<S*>(MODE == kModeGram ? d.A : MODE == kModePoly ? d.B
                                              : (ep.cur ? d.X0 : d.X1));
+  const S* ein = MODE == kModePoly ? static_cast<const S*>(d.A) : Xcur;  // epilogue input
+  S* W = static_cast<S*>(d.W);
   const int ldo = sym ? d.m_pad : d.n_pad;
   const bool vec = d.vec_ok != 0;
 
+  // pass A coordinates of iteration p: tile row, tile column, staged slice
+  auto coordA = [&](int i, int p, int& grow, int& gcol, int& sl, int& r_in, int& c_in) {
+    const int it = p * kThreads + tid;
+    const int rr = it >> 5, cv = it & 31;
+    const int wrr = rr >> 5, wcc = cv >> 4;
+    r_in = rr & 31;
+    c_in = (cv & 15) * 8;
+    sl = wrr * 2 + wcc;
+    grow = row0 + wrr * 128 + i * 32 + r_in;
+    gcol = col0 + wcc * 128 + c_in;
+  };
+
+  // One 64 x 256 block per accumulator row i; i is a compile-time constant
+  // so that acc stays in registers.
+  auto block = [&](auto i_c) {
+    constexpr int i = decltype(i_c)::value;
+    // global inputs of pass A, issued before the staging so that their
+    // latency overlaps it
+    Raw8 xin[8], win[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int p = 0; p < 8; ++p) {
+      int grow, gcol, sl, r_in, c_in;
+      coordA(i, p, grow, gcol, sl, r_in, c_in);
+      if (MODE != kModeGram) xin[p] = load_raw8<E>(ein + static_cast<size_t>(grow) * ldo + gcol);
+      if (MODE == kModeApply && wide_apply && vec && grow < d.m && gcol + 8 <= d.n)
+        win[p] = load_raw8<E>(W + static_cast<size_t>(grow) * d.cols + gcol);
+    }
     {
-      float* reg = stage + wave * WREG;
+      float* reg = slice_of(wave);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          reg[((r >> 2) * 8 + lhalf * 4 + (r & 3)) * SP + j * 32 + lrow] = acc[i][j][r];
+          reg[sidx((r >> 2) * 8 + lhalf * 4 + (r & 3), j * 32 + lrow)] = acc[i][j][r];
     }
     __syncthreads();
 
     // Pass A: row-major, eight consecutive columns per thread.
+#pragma unroll
     for (int p = 0; p < 8; ++p) {
-      const int it = p * kThreads + tid;
-      const int rr = it >> 5, cv = it & 31;
-      const int wrr = rr >> 5, r_in = rr & 31, wcc = cv >> 4, c_in = (cv & 15) * 8;
-      float* src = stage + (wrr * 2 + wcc) * WREG + r_in * SP + c_in;
-      const float4 lo = *reinterpret_cast<const float4*>(src);
-      const float4 hi = *reinterpret_cast<const float4*>(src + 4);
+      int grow, gcol, sl, r_in, c_in;
+      coordA(i, p, grow, gcol, sl, r_in, c_in);
+      float* slice = slice_of(sl);
+      float* src_lo = slice + sidx(r_in, c_in);
+      float* src_hi = slice + sidx(r_in, c_in + 4);
+      const float4 lo = *reinterpret_cast<const float4*>(src_lo);
+      const float4 hi = *reinterpret_cast<const float4*>(src_hi);
       float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      const int grow = row0 + wrr * 128 + i * 32 + r_in;
-      const int gcol = col0 + wcc * 128 + c_in;
       const size_t goff = static_cast<size_t>(grow) * ldo + gcol;
       if (MODE == kModeGram) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= alpha;
-      } else if (MODE == kModePoly) {
-        float a8[8];
-        load8<E>(static_cast<const S*>(d.A) + goff, a8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = fmaf(ep.c, v[e], ep.b * a8[e]);
       } else {
         float x8[8];
-        load8<E>(Xcur + goff, x8);
+        unpack_raw8<E>(xin[p], x8);
+        if (MODE == kModePoly) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = alpha * fmaf(ep.kb, v[e], ep.a * x8[e]);
+          for (int e = 0; e < 8; ++e) v[e] = fmaf(ep.c, v[e], ep.b * x8[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = alpha * fmaf(ep.kb, v[e], ep.a * x8[e]);
+        }
       }
-      if (MODE != kModeUpdate || !ep.last) {
+      if constexpr (MODE != kModeApply) {
         store8<E>(out + goff, v);
-      } else if (!d.tall) {
-        if (grow < d.m && gcol < d.n)
-          apply8<E>(d, static_cast<size_t>(grow) * d.cols + gcol, min(8, d.n - gcol), vec, v,
-                    ep.decay);
+      } else if (wide_apply && grow < d.m && gcol < d.n) {
+        const size_t uo = static_cast<size_t>(grow) * d.cols + gcol;
+        if (vec && gcol + 8 <= d.n)
+          apply8_vec<E>(d, uo, win[p], v, ep.decay);
+        else
+          apply8_scalar<E>(d, uo, min(8, d.n - gcol), v, ep.decay);
       }
-      if (mirror || tall_apply) {
-        *reinterpret_cast<float4*>(src) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(src + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      if ((sym && mirror) || (MODE == kModeApply && tall_apply)) {
+        *reinterpret_cast<float4*>(src_lo) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(src_hi) = make_float4(v[4], v[5], v[6], v[7]);
       }
     }
 
     // Pass B: column-wise, eight consecutive tile rows of one tile column.
-    if (mirror || tall_apply) {
+    if ((sym || MODE == kModeApply) && (mirror || tall_apply)) {
       __syncthreads();
-      for (int p = 0; p < 8; ++p) {
+      auto coordB = [&](int p, int& gcol, int& grow0, int& sl, int& sub, int& c_in) {
         const int it = p * kThreads + tid;
         const int tc = it >> 3, q = it & 7;
-        const int wrr = q >> 2, sub = q & 3, wcc = tc >> 7, c_in = tc & 127;
-        const float* src = stage + (wrr * 2 + wcc) * WREG + (sub * 8) * SP + c_in;
+        const int wrr = q >> 2, wcc = tc >> 7;
+        sub = q & 3;
+        c_in = tc & 127;
+        sl = wrr * 2 + wcc;
+        grow0 = row0 + wrr * 128 + i * 32 + sub * 8;
+        gcol = col0 + tc;
+      };
+      if (MODE == kModeApply && tall_apply) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          int gcol, grow0, sl, sub, c_in;
+          coordB(p, gcol, grow0, sl, sub, c_in);
+          if (vec && gcol < d.n && grow0 + 8 <= d.m)
+            win[p] = load_raw8<E>(W + static_cast<size_t>(gcol) * d.cols + grow0);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        int gcol, grow0, sl, sub, c_in;
+        coordB(p, gcol, grow0, sl, sub, c_in);
+        const float* slice = slice_of(sl);
         float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = src[e * SP];
-        const int grow0 = row0 + wrr * 128 + i * 32 + sub * 8;
-        const int gcol = col0 + tc;
-        if (mirror) {
+        for (int e = 0; e < 8; ++e) v[e] = slice[sidx(sub * 8 + e, c_in)];
+        if constexpr (sym) {
           store8<E>(out + static_cast<size_t>(gcol) * ldo + grow0, v);
-        } else if (gcol < d.n && grow0 < d.m) {
-          apply8<E>(d, static_cast<size_t>(gcol) * d.cols + grow0, min(8, d.m - grow0), vec, v,
-                    ep.decay);
+        } else if (MODE == kModeApply && gcol < d.n && grow0 < d.m) {
+          const size_t uo = static_cast<size_t>(gcol) * d.cols + grow0;
+          if (vec && grow0 + 8 <= d.m)
+            apply8_vec<E>(d, uo, win[p], v, ep.decay);
+          else
+            apply8_scalar<E>(d, uo, min(8, d.m - grow0), v, ep.decay);
         }
       }
     }
     __syncthreads();
-  }
+  };
+  block(std::integral_constant<int, 0>{});
+  block(std::integral_constant<int, 1>{});
+  block(std::integral_constant<int, 2>{});
+  block(std::integral_constant<int, 3>{});
 }
 
 }  // namespace mfsdp
