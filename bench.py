@@ -33,7 +33,7 @@ METRIC = "owner-local Muon step ms and Newton-Schulz TFLOP/s (% bf16 MFMA peak)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
-KINDS = ("momentum", "norm", "gram", "poly", "update", "apply", "adamw")
+KINDS = ("momentum", "norm", "gram", "poly", "update", "final", "apply", "adamw")
 
 
 def ns_flops_by_kind(shapes):
@@ -170,7 +170,7 @@ def main():
 
     flops = ns_flops_by_kind(shapes)
     ns_flops_step = wl.ns_steps * sum(flops.values())
-    ns_kernel_ms = sum(per_kind[k]["ms_per_step"] for k in ("gram", "poly", "update")
+    ns_kernel_ms = sum(per_kind[k]["ms_per_step"] for k in ("gram", "poly", "update", "final")
                        if k in per_kind)
     peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_FP32_MFMA_TFLOPS
     dominant = max(per_kind, key=lambda k: per_kind[k]["ms_per_step"])

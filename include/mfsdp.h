@@ -170,10 +170,11 @@ typedef enum mfsdp_kernel_kind {
   MFSDP_KERNEL_NORM = 1,      /* per-matrix norm finalization        */
   MFSDP_KERNEL_GRAM = 2,      /* A = X X^T                           */
   MFSDP_KERNEL_POLY = 3,      /* B = b A + c A A                     */
-  MFSDP_KERNEL_UPDATE = 4,    /* X = a X + B X (last one applies W)  */
+  MFSDP_KERNEL_UPDATE = 4,    /* X = a X + B X, all but the last     */
   MFSDP_KERNEL_APPLY = 5,     /* apply when ns_steps == 0            */
   MFSDP_KERNEL_ADAMW = 6,     /* AdamW tail                          */
-  MFSDP_KERNEL_KINDS = 7
+  MFSDP_KERNEL_FINAL = 7,     /* last update, applies W (2 launches) */
+  MFSDP_KERNEL_KINDS = 8
 } mfsdp_kernel_kind_t;
 
 mfsdp_status_t mfsdp_timing_enable(int enable);

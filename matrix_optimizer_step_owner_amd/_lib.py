@@ -17,7 +17,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 NS_EPS = 1e-7
 KERNEL_KINDS = {"momentum": 0, "norm": 1, "gram": 2, "poly": 3, "update": 4,
-                "apply": 5, "adamw": 6}
+                "apply": 5, "adamw": 6, "final": 7}
 
 #: Every symbol include/mfsdp.h declares.
 EXPORTED = ("mfsdp_muon_workspace_size", "mfsdp_muon_step", "mfsdp_adamw_tail",

@@ -128,6 +128,7 @@ struct Plan {
   std::vector<size_t> off_x0, off_x1, off_a, off_b;
   size_t total = 0;
   int64_t ew_total = 0, gram_total = 0, upd_total = 0;
+  int64_t upd_wide_total = 0;       // tiles of matrices stored wide (rows <= cols)
 };
 
 mfsdp_status_t make_geom(const mfsdp_matrix_t& mt, int64_t idx, MatGeom* g) {
@@ -160,6 +161,7 @@ mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t d
     const int64_t tm = p->geom[i].m_pad / kTile, tn = p->geom[i].n_pad / kTile;
     p->gram_total += tm * (tm + 1) / 2;
     p->upd_total += tm * tn;
+    if (!p->geom[i].tall) p->upd_wide_total += tm * tn;
   }
   if (p->ew_total >= (int64_t(1) << 31) || p->upd_total >= (int64_t(1) << 31))
     return fail(MFSDP_ERR_UNSUPPORTED, "too many tiles in one call");
@@ -171,7 +173,9 @@ mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t d
   off = align_up(off + 3 * (2 * n + 1) * sizeof(int32_t), kWsAlign);
   // per-tile (matrix, tile) tables of the symmetric and update launches
   p->off_tiles = off;
-  off = align_up(off + (p->gram_total + p->upd_total) * sizeof(int2), kWsAlign);
+  // tables: symmetric launches, updates, then the final update split into
+  // wide-matrix tiles followed by tall-matrix tiles
+  off = align_up(off + (p->gram_total + 2 * p->upd_total) * sizeof(int2), kWsAlign);
   p->blob_bytes = off;
   p->off_scales = off;
   off = align_up(off + n * sizeof(float), kWsAlign);
@@ -247,6 +251,9 @@ hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nest
   const WorkList wl_ew = list(0);
   const int2* tiles_sym = reinterpret_cast<const int2*>(ws + p.off_tiles);
   const int2* tiles_upd = tiles_sym + p.gram_total;
+  const int2* tiles_fin_wide = tiles_upd + p.upd_total;
+  const int2* tiles_fin_tall = tiles_fin_wide + p.upd_wide_total;
+  const int64_t fin_tall_total = p.upd_total - p.upd_wide_total;
   float* scales = reinterpret_cast<float*>(ws + p.off_scales);
   double* partials = reinterpret_cast<double*>(ws + p.off_partials);
 
@@ -291,15 +298,28 @@ hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nest
       });
       if (e != hipSuccess) return e;
     }
-    const bool last = it == ns_steps - 1;
-    e = launch(MFSDP_KERNEL_UPDATE, stream, [&] {
-      if (last)
-        ns_gemm_kernel<E, kModeApply><<<dim3(static_cast<unsigned>(p.upd_total)), dim3(kThreads),
-                                        0, stream>>>(descs, tiles_upd, scales, ep);
-      else
+    if (it + 1 < ns_steps) {
+      e = launch(MFSDP_KERNEL_UPDATE, stream, [&] {
         ns_gemm_kernel<E, kModeUpdate><<<dim3(static_cast<unsigned>(p.upd_total)), dim3(kThreads),
                                          0, stream>>>(descs, tiles_upd, scales, ep);
-    });
+      });
+    } else {
+      if (p.upd_wide_total > 0) {
+        e = launch(MFSDP_KERNEL_FINAL, stream, [&] {
+          ns_gemm_kernel<E, kModeApplyWide><<<dim3(static_cast<unsigned>(p.upd_wide_total)),
+                                              dim3(kThreads), 0, stream>>>(
+              descs, tiles_fin_wide, scales, ep);
+        });
+        if (e != hipSuccess) return e;
+      }
+      if (fin_tall_total > 0) {
+        e = launch(MFSDP_KERNEL_FINAL, stream, [&] {
+          ns_gemm_kernel<E, kModeApplyTall><<<dim3(static_cast<unsigned>(fin_tall_total)),
+                                              dim3(kThreads), 0, stream>>>(
+              descs, tiles_fin_tall, scales, ep);
+        });
+      }
+    }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -466,6 +486,13 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
       for (int64_t it = 0; it < n_mats; ++it)
         for (int32_t t = 0; t < begin[it + 1] - begin[it]; ++t) *tab++ = make_int2(mat[it], t);
     }
+    // final update: the update list's wide matrices, then its tall ones
+    const int32_t* mat = lists + 2 * (2 * n_mats + 1);
+    const int32_t* begin = mat + n_mats;
+    for (int tall = 0; tall <= 1; ++tall)
+      for (int64_t it = 0; it < n_mats; ++it)
+        if (p.geom[mat[it]].tall == (tall == 1))
+          for (int32_t t = 0; t < begin[it + 1] - begin[it]; ++t) *tab++ = make_int2(mat[it], t);
   }
 
   hipError_t e = hipMemcpyAsync(ws, blob.data(), p.blob_bytes, hipMemcpyHostToDevice, stream);

@@ -25,10 +25,18 @@
 
 namespace mfsdp {
 
-// kModeUpdate writes the next iterate; kModeApply is the update of the last
-// iteration, which applies W (and update_out) instead.  Separate kernels keep
-// the apply code out of the update that runs on every other iteration.
-enum NsMode { kModeGram = 0, kModePoly = 1, kModeUpdate = 2, kModeApply = 3 };
+// kModeUpdate writes the next iterate.  The update of the last iteration
+// applies W (and update_out) instead: kModeApplyWide for matrices stored
+// wide (rows <= cols, row-major apply), kModeApplyTall for tall ones (the
+// transposed apply).  Separate kernels keep each one's code small: the
+// epilogue runs once per tile and is fetched into the instruction cache anew.
+enum NsMode {
+  kModeGram = 0,
+  kModePoly = 1,
+  kModeUpdate = 2,
+  kModeApplyWide = 3,
+  kModeApplyTall = 4
+};
 
 struct NsEpi {
   int cur;        // 0: the current iterate is X0, 1: X1
@@ -225,7 +233,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   const int local = tile.y;
   const MatDesc d = descs[k];
 
-  constexpr bool kUpd = MODE == kModeUpdate || MODE == kModeApply;
+  constexpr bool kApply = MODE == kModeApplyWide || MODE == kModeApplyTall;
+  constexpr bool kUpd = MODE == kModeUpdate || kApply;
   int ti, tj;
   if (kUpd) {
     const int tn = d.n_pad / kTile;
@@ -439,8 +448,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   const float s_norm = scales[k];
   constexpr bool sym = !kUpd;
   const bool mirror = sym && ti != tj;
-  const bool wide_apply = MODE == kModeApply && !d.tall;
-  const bool tall_apply = MODE == kModeApply && d.tall;
+  constexpr bool wide_apply = MODE == kModeApplyWide;
+  constexpr bool tall_apply = MODE == kModeApplyTall;
   const float alpha = MODE == kModeGram ? (ep.first ? s_norm * s_norm : 1.f)
                     : kUpd ? (ep.first ? s_norm : 1.f) : 1.f;
   S* out = static_cast<S*>(MODE == kModeGram ? d.A : MODE == kModePoly ? d.B
@@ -474,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
       int grow, gcol, sl, r_in, c_in;
       coordA(i, p, grow, gcol, sl, r_in, c_in);
       if (MODE != kModeGram) xin[p] = load_raw8<E>(ein + static_cast<size_t>(grow) * ldo + gcol);
-      if (MODE == kModeApply && wide_apply && vec && grow < d.m && gcol + 8 <= d.n)
+      if (wide_apply && vec && grow < d.m && gcol + 8 <= d.n)
         win[p] = load_raw8<E>(W + static_cast<size_t>(grow) * d.cols + gcol);
     }
     {
@@ -513,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
           for (int e = 0; e < 8; ++e) v[e] = alpha * fmaf(ep.kb, v[e], ep.a * x8[e]);
         }
       }
-      if constexpr (MODE != kModeApply) {
+      if constexpr (!kApply) {
         store8<E>(out + goff, v);
       } else if (wide_apply && grow < d.m && gcol < d.n) {
         const size_t uo = static_cast<size_t>(grow) * d.cols + gcol;
@@ -522,14 +531,14 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
         else
           apply8_scalar<E>(d, uo, min(8, d.n - gcol), v, ep.decay);
       }
-      if ((sym && mirror) || (MODE == kModeApply && tall_apply)) {
+      if (mirror || tall_apply) {
         *reinterpret_cast<float4*>(src_lo) = make_float4(v[0], v[1], v[2], v[3]);
         *reinterpret_cast<float4*>(src_hi) = make_float4(v[4], v[5], v[6], v[7]);
       }
     }
 
     // Pass B: column-wise, eight consecutive tile rows of one tile column.
-    if ((sym || MODE == kModeApply) && (mirror || tall_apply)) {
+    if (mirror || tall_apply) {
       __syncthreads();
       auto coordB = [&](int p, int& gcol, int& grow0, int& sl, int& sub, int& c_in) {
         const int it = p * kThreads + tid;
@@ -541,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
         grow0 = row0 + wrr * 128 + i * 32 + sub * 8;
         gcol = col0 + tc;
       };
-      if (MODE == kModeApply && tall_apply) {
+      if constexpr (tall_apply) {
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
           int gcol, grow0, sl, sub, c_in;
@@ -560,7 +569,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
         for (int e = 0; e < 8; ++e) v[e] = slice[sidx(sub * 8 + e, c_in)];
         if constexpr (sym) {
           store8<E>(out + static_cast<size_t>(gcol) * ldo + grow0, v);
-        } else if (MODE == kModeApply && gcol < d.n && grow0 < d.m) {
+        } else if (tall_apply && gcol < d.n && grow0 < d.m) {
           const size_t uo = static_cast<size_t>(gcol) * d.cols + grow0;
           if (vec && grow0 + 8 <= d.m)
             apply8_vec<E>(d, uo, win[p], v, ep.decay);
