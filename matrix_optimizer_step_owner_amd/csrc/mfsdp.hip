@@ -15,6 +15,8 @@
 #include <cstdio>
 #include <cstring>
 #include <exception>
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -128,8 +130,38 @@ struct Plan {
   std::vector<size_t> off_x0, off_x1, off_a, off_b;
   size_t total = 0;
   int64_t ew_total = 0, gram_total = 0, upd_total = 0;
-  int64_t upd_wide_total = 0;       // tiles of matrices stored wide (rows <= cols)
+  // Newton-Schulz groups: matrices split into flop-balanced groups whose
+  // iterations run on separate streams (see enqueue_muon).  Per group: its
+  // matrices and the offsets/counts of its tile tables (in int2 entries from
+  // off_tiles): symmetric, update, final-wide, final-tall.
+  struct Group {
+    std::vector<int64_t> mats;
+    int64_t sym = 0, upd = 0, fin_wide = 0, fin_tall = 0;
+    int64_t t_sym = 0, t_upd = 0, t_fin_wide = 0, t_fin_tall = 0;
+  };
+  std::vector<Group> groups;
 };
+
+// Work-group count that one launch needs to fill the MI355X (256 CUs).
+constexpr int64_t kCus = 256;
+constexpr int kMaxGroups = 4;
+
+// Number of Newton-Schulz groups for a call: one when a single grouped launch
+// already has many rounds of tiles, more when few rounds would leave CUs idle
+// at the end of each launch.  MFSDP_NS_GROUPS overrides it (debugging).
+int choose_groups(int64_t n, int64_t upd_total) {
+  int g;
+  const int64_t rounds = upd_total / kCus;
+  if (upd_total < kCus / 4) g = 1;          // latency-bound; not worth streams
+  else if (rounds >= 6) g = 1;
+  else if (rounds >= 2) g = 2;
+  else g = 3;
+  if (const char* env = getenv("MFSDP_NS_GROUPS")) {
+    const int v = atoi(env);
+    if (v >= 1 && v <= kMaxGroups) g = v;
+  }
+  return static_cast<int>(std::min<int64_t>(g, n));
+}
 
 mfsdp_status_t make_geom(const mfsdp_matrix_t& mt, int64_t idx, MatGeom* g) {
   if (mt.rows < 1 || mt.cols < 1)
@@ -161,7 +193,42 @@ mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t d
     const int64_t tm = p->geom[i].m_pad / kTile, tn = p->geom[i].n_pad / kTile;
     p->gram_total += tm * (tm + 1) / 2;
     p->upd_total += tm * tn;
-    if (!p->geom[i].tall) p->upd_wide_total += tm * tn;
+  }
+  // flop-balanced groups (largest first onto the least loaded group)
+  {
+    const int ng = choose_groups(n, p->upd_total);
+    p->groups.assign(ng, Plan::Group{});
+    std::vector<int64_t> order(n), work(n);
+    std::vector<int64_t> load(ng, 0);
+    for (int64_t i = 0; i < n; ++i) {
+      const MatGeom& g = p->geom[i];
+      const int64_t tm = g.m_pad / kTile, tn = g.n_pad / kTile;
+      work[i] = tm * (tm + 1) / 2 * (g.n_pad + g.m_pad) + tm * tn * g.m_pad;
+      order[i] = i;
+    }
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int64_t a, int64_t b) { return work[a] > work[b]; });
+    for (int64_t i : order) {
+      const int gi = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
+      load[gi] += work[i];
+      p->groups[gi].mats.push_back(i);
+    }
+    int64_t off_t = 0;
+    for (Plan::Group& gr : p->groups) {
+      std::sort(gr.mats.begin(), gr.mats.end());
+      for (int64_t i : gr.mats) {
+        const MatGeom& g = p->geom[i];
+        const int64_t tm = g.m_pad / kTile, tn = g.n_pad / kTile;
+        gr.sym += tm * (tm + 1) / 2;
+        gr.upd += tm * tn;
+        if (g.tall) gr.fin_tall += tm * tn; else gr.fin_wide += tm * tn;
+      }
+      gr.t_sym = off_t;
+      gr.t_upd = gr.t_sym + gr.sym;
+      gr.t_fin_wide = gr.t_upd + gr.upd;
+      gr.t_fin_tall = gr.t_fin_wide + gr.fin_wide;
+      off_t = gr.t_fin_tall + gr.fin_tall;
+    }
   }
   if (p->ew_total >= (int64_t(1) << 31) || p->upd_total >= (int64_t(1) << 31))
     return fail(MFSDP_ERR_UNSUPPORTED, "too many tiles in one call");
@@ -169,12 +236,11 @@ mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t d
   p->off_descs = off;
   off = align_up(off + n * sizeof(MatDesc), kWsAlign);
   p->off_lists = off;
-  // three work lists (momentum, symmetric products, update): mat[n], begin[n+1]
-  off = align_up(off + 3 * (2 * n + 1) * sizeof(int32_t), kWsAlign);
-  // per-tile (matrix, tile) tables of the symmetric and update launches
+  // momentum work list: mat[n], begin[n+1]
+  off = align_up(off + (2 * n + 1) * sizeof(int32_t), kWsAlign);
+  // per-tile (matrix, tile) tables, per group: symmetric launches, updates,
+  // final update over wide matrices, final update over tall matrices
   p->off_tiles = off;
-  // tables: symmetric launches, updates, then the final update split into
-  // wide-matrix tiles followed by tall-matrix tiles
   off = align_up(off + (p->gram_total + 2 * p->upd_total) * sizeof(int2), kWsAlign);
   p->blob_bytes = off;
   p->off_scales = off;
@@ -218,42 +284,112 @@ mfsdp_status_t check_aliasing(std::vector<Range>& rs) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Work list: items sorted by `key` descending (largest K first).
-void fill_list(int32_t* mat, int32_t* begin, const std::vector<int64_t>& tiles,
-               const std::vector<int64_t>& key) {
-  const int64_t n = static_cast<int64_t>(tiles.size());
-  std::vector<int64_t> order(n);
-  for (int64_t i = 0; i < n; ++i) order[i] = i;
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int64_t a, int64_t b) { return key[a] > key[b]; });
-  int64_t acc = 0;
-  for (int64_t i = 0; i < n; ++i) {
-    mat[i] = static_cast<int32_t>(order[i]);
-    begin[i] = static_cast<int32_t>(acc);
-    acc += tiles[order[i]];
+// Per-device pool of auxiliary streams and fork/join events for the
+// Newton-Schulz groups.  Created on first use, kept until the process ends
+// (host objects; no device memory).  Every stream has the default priority.
+struct StreamPool {
+  hipStream_t aux[kMaxGroups - 1] = {};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[kMaxGroups - 1] = {};
+};
+
+std::mutex g_pool_mu;
+std::map<int, StreamPool> g_pools;
+
+hipError_t get_pool(StreamPool** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  auto it = g_pools.find(dev);
+  if (it == g_pools.end()) {
+    StreamPool sp;
+    for (int i = 0; i < kMaxGroups - 1; ++i) {
+      e = hipStreamCreateWithFlags(&sp.aux[i], hipStreamNonBlocking);
+      if (e != hipSuccess) return e;
+      e = hipEventCreateWithFlags(&sp.join[i], hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+    e = hipEventCreateWithFlags(&sp.fork, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    it = g_pools.emplace(dev, sp).first;
   }
-  begin[n] = static_cast<int32_t>(acc);
+  *out = &it->second;
+  return hipSuccess;
 }
 
+// Newton-Schulz iterations of one group on one stream.
+template <class E>
+hipError_t enqueue_ns_group(const Plan& p, const Plan::Group& gr, const MatDesc* descs,
+                            const int2* tiles, const float* scales, float decay, int ns_steps,
+                            float a, float b, float c, hipStream_t stream) {
+  const bool skip_poly = (c == 0.f);
+  hipError_t e = hipSuccess;
+  for (int it = 0; it < ns_steps; ++it) {
+    NsEpi ep;
+    ep.cur = it & 1;
+    ep.first = it == 0;
+    ep.b_is_A = skip_poly ? 1 : 0;
+    ep.a = a;
+    ep.b = b;
+    ep.c = c;
+    ep.kb = skip_poly ? b : 1.f;
+    ep.decay = decay;
+    e = launch(MFSDP_KERNEL_GRAM, stream, [&] {
+      ns_gemm_kernel<E, kModeGram><<<dim3(static_cast<unsigned>(gr.sym)), dim3(kThreads), 0,
+                                     stream>>>(descs, tiles + gr.t_sym, scales, ep);
+    });
+    if (e != hipSuccess) return e;
+    if (!skip_poly) {
+      e = launch(MFSDP_KERNEL_POLY, stream, [&] {
+        ns_gemm_kernel<E, kModePoly><<<dim3(static_cast<unsigned>(gr.sym)), dim3(kThreads), 0,
+                                       stream>>>(descs, tiles + gr.t_sym, scales, ep);
+      });
+      if (e != hipSuccess) return e;
+    }
+    if (it + 1 < ns_steps) {
+      e = launch(MFSDP_KERNEL_UPDATE, stream, [&] {
+        ns_gemm_kernel<E, kModeUpdate><<<dim3(static_cast<unsigned>(gr.upd)), dim3(kThreads), 0,
+                                         stream>>>(descs, tiles + gr.t_upd, scales, ep);
+      });
+      if (e != hipSuccess) return e;
+    } else {
+      if (gr.fin_wide > 0) {
+        e = launch(MFSDP_KERNEL_FINAL, stream, [&] {
+          ns_gemm_kernel<E, kModeApplyWide><<<dim3(static_cast<unsigned>(gr.fin_wide)),
+                                              dim3(kThreads), 0, stream>>>(
+              descs, tiles + gr.t_fin_wide, scales, ep);
+        });
+        if (e != hipSuccess) return e;
+      }
+      if (gr.fin_tall > 0) {
+        e = launch(MFSDP_KERNEL_FINAL, stream, [&] {
+          ns_gemm_kernel<E, kModeApplyTall><<<dim3(static_cast<unsigned>(gr.fin_tall)),
+                                              dim3(kThreads), 0, stream>>>(
+              descs, tiles + gr.t_fin_tall, scales, ep);
+        });
+        if (e != hipSuccess) return e;
+      }
+    }
+  }
+  return e;
+}
+
+// Whole step.  Momentum and norm run on the caller's stream; then the
+// Newton-Schulz groups fork onto the caller's stream plus auxiliary streams
+// (their launches overlap, so one group's partial last round of tiles is
+// filled by another group's tiles) and join back before returning.  Results
+// do not depend on the grouping: every matrix is computed the same way.
 template <class E>
 hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nesterov,
                         float decay, int ns_steps, float a, float b, float c,
                         hipStream_t stream) {
   const MatDesc* descs = reinterpret_cast<const MatDesc*>(ws + p.off_descs);
   const int32_t* lists = reinterpret_cast<const int32_t*>(ws + p.off_lists);
-  auto list = [&](int which) {
-    WorkList wl;
-    wl.mat = lists + which * (2 * n + 1);
-    wl.begin = wl.mat + n;
-    wl.n_items = static_cast<int32_t>(n);
-    return wl;
-  };
-  const WorkList wl_ew = list(0);
-  const int2* tiles_sym = reinterpret_cast<const int2*>(ws + p.off_tiles);
-  const int2* tiles_upd = tiles_sym + p.gram_total;
-  const int2* tiles_fin_wide = tiles_upd + p.upd_total;
-  const int2* tiles_fin_tall = tiles_fin_wide + p.upd_wide_total;
-  const int64_t fin_tall_total = p.upd_total - p.upd_wide_total;
+  WorkList wl_ew;
+  wl_ew.mat = lists;
+  wl_ew.begin = lists + n;
+  wl_ew.n_items = static_cast<int32_t>(n);
+  const int2* tiles = reinterpret_cast<const int2*>(ws + p.off_tiles);
   float* scales = reinterpret_cast<float*>(ws + p.off_scales);
   double* partials = reinterpret_cast<double*>(ws + p.off_partials);
 
@@ -275,51 +411,30 @@ hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nest
     });
   }
 
-  const bool skip_poly = (c == 0.f);
-  for (int it = 0; it < ns_steps; ++it) {
-    NsEpi ep;
-    ep.cur = it & 1;
-    ep.first = it == 0;
-    ep.b_is_A = skip_poly ? 1 : 0;
-    ep.a = a;
-    ep.b = b;
-    ep.c = c;
-    ep.kb = skip_poly ? b : 1.f;
-    ep.decay = decay;
-    e = launch(MFSDP_KERNEL_GRAM, stream, [&] {
-      ns_gemm_kernel<E, kModeGram><<<dim3(static_cast<unsigned>(p.gram_total)), dim3(kThreads), 0,
-                                     stream>>>(descs, tiles_sym, scales, ep);
-    });
+  const int ng = static_cast<int>(p.groups.size());
+  if (ng == 1)
+    return enqueue_ns_group<E>(p, p.groups[0], descs, tiles, scales, decay, ns_steps, a, b, c,
+                               stream);
+
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  StreamPool* pool = nullptr;
+  e = get_pool(&pool);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(pool->fork, stream);
+  if (e != hipSuccess) return e;
+  for (int g = 1; g < ng; ++g) {
+    e = hipStreamWaitEvent(pool->aux[g - 1], pool->fork, 0);
     if (e != hipSuccess) return e;
-    if (!skip_poly) {
-      e = launch(MFSDP_KERNEL_POLY, stream, [&] {
-        ns_gemm_kernel<E, kModePoly><<<dim3(static_cast<unsigned>(p.gram_total)), dim3(kThreads), 0,
-                                       stream>>>(descs, tiles_sym, scales, ep);
-      });
-      if (e != hipSuccess) return e;
-    }
-    if (it + 1 < ns_steps) {
-      e = launch(MFSDP_KERNEL_UPDATE, stream, [&] {
-        ns_gemm_kernel<E, kModeUpdate><<<dim3(static_cast<unsigned>(p.upd_total)), dim3(kThreads),
-                                         0, stream>>>(descs, tiles_upd, scales, ep);
-      });
-    } else {
-      if (p.upd_wide_total > 0) {
-        e = launch(MFSDP_KERNEL_FINAL, stream, [&] {
-          ns_gemm_kernel<E, kModeApplyWide><<<dim3(static_cast<unsigned>(p.upd_wide_total)),
-                                              dim3(kThreads), 0, stream>>>(
-              descs, tiles_fin_wide, scales, ep);
-        });
-        if (e != hipSuccess) return e;
-      }
-      if (fin_tall_total > 0) {
-        e = launch(MFSDP_KERNEL_FINAL, stream, [&] {
-          ns_gemm_kernel<E, kModeApplyTall><<<dim3(static_cast<unsigned>(fin_tall_total)),
-                                              dim3(kThreads), 0, stream>>>(
-              descs, tiles_fin_tall, scales, ep);
-        });
-      }
-    }
+  }
+  for (int g = 0; g < ng; ++g) {
+    hipStream_t s = g == 0 ? stream : pool->aux[g - 1];
+    e = enqueue_ns_group<E>(p, p.groups[g], descs, tiles, scales, decay, ns_steps, a, b, c, s);
+    if (e != hipSuccess) return e;
+  }
+  for (int g = 1; g < ng; ++g) {
+    e = hipEventRecord(pool->join[g - 1], pool->aux[g - 1]);
+    if (e != hipSuccess) return e;
+    e = hipStreamWaitEvent(stream, pool->join[g - 1], 0);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -427,8 +542,6 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
   std::vector<char> blob(p.blob_bytes, 0);
   MatDesc* descs = reinterpret_cast<MatDesc*>(blob.data() + p.off_descs);
   int32_t* lists = reinterpret_cast<int32_t*>(blob.data() + p.off_lists);
-  std::vector<int64_t> t_ew(n_mats), t_sym(n_mats), t_upd(n_mats), k_gram(n_mats), k_upd(n_mats),
-      zero(n_mats, 0);
   int64_t ew_acc = 0;
   for (int64_t i = 0; i < n_mats; ++i) {
     const MatGeom& g = p.geom[i];
@@ -455,12 +568,6 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
     d.lr_scale = lr * mt.scale;
     d.vec_ok = (g.cols % static_cast<int64_t>(16 / es)) == 0 ? 1 : 0;
     ew_acc += g.ew_ntiles;
-    const int64_t tm = g.m_pad / kTile, tn = g.n_pad / kTile;
-    t_ew[i] = g.ew_ntiles;
-    t_sym[i] = tm * (tm + 1) / 2;
-    t_upd[i] = tm * tn;
-    k_gram[i] = g.n_pad;
-    k_upd[i] = g.m_pad;
   }
   // momentum tiles in list order: partial sums of a matrix stay contiguous
   // in the order the finalization reads them.
@@ -471,28 +578,43 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
     for (int64_t i = 0; i < n_mats; ++i) {
       mat[i] = static_cast<int32_t>(i);
       begin[i] = static_cast<int32_t>(acc);
-      acc += t_ew[i];
+      acc += p.geom[i].ew_ntiles;
     }
     begin[n_mats] = static_cast<int32_t>(acc);
   }
-  fill_list(lists + (2 * n_mats + 1), lists + (2 * n_mats + 1) + n_mats, t_sym, k_gram);
-  fill_list(lists + 2 * (2 * n_mats + 1), lists + 2 * (2 * n_mats + 1) + n_mats, t_upd, k_upd);
+  // per-group tile tables; within a launch, matrices with the longest K
+  // first (they are dispatched first and set the launch's critical path)
   {
-    // expand the two GEMM work lists into per-tile tables
     int2* tab = reinterpret_cast<int2*>(blob.data() + p.off_tiles);
-    for (int which = 1; which <= 2; ++which) {
-      const int32_t* mat = lists + which * (2 * n_mats + 1);
-      const int32_t* begin = mat + n_mats;
-      for (int64_t it = 0; it < n_mats; ++it)
-        for (int32_t t = 0; t < begin[it + 1] - begin[it]; ++t) *tab++ = make_int2(mat[it], t);
+    for (const Plan::Group& gr : p.groups) {
+      std::vector<int64_t> by_n(gr.mats), by_m(gr.mats);
+      std::stable_sort(by_n.begin(), by_n.end(), [&](int64_t x, int64_t y) {
+        return p.geom[x].n_pad > p.geom[y].n_pad;
+      });
+      std::stable_sort(by_m.begin(), by_m.end(), [&](int64_t x, int64_t y) {
+        return p.geom[x].m_pad > p.geom[y].m_pad;
+      });
+      int2* t = tab + gr.t_sym;
+      for (int64_t i : by_n) {
+        const int64_t tm = p.geom[i].m_pad / kTile;
+        for (int64_t q = 0; q < tm * (tm + 1) / 2; ++q)
+          *t++ = make_int2(static_cast<int>(i), static_cast<int>(q));
+      }
+      t = tab + gr.t_upd;
+      for (int64_t i : by_m) {
+        const int64_t nt = (p.geom[i].m_pad / kTile) * (p.geom[i].n_pad / kTile);
+        for (int64_t q = 0; q < nt; ++q) *t++ = make_int2(static_cast<int>(i), static_cast<int>(q));
+      }
+      for (int tall = 0; tall <= 1; ++tall) {
+        t = tab + (tall ? gr.t_fin_tall : gr.t_fin_wide);
+        for (int64_t i : by_m) {
+          if (p.geom[i].tall != (tall == 1)) continue;
+          const int64_t nt = (p.geom[i].m_pad / kTile) * (p.geom[i].n_pad / kTile);
+          for (int64_t q = 0; q < nt; ++q)
+            *t++ = make_int2(static_cast<int>(i), static_cast<int>(q));
+        }
+      }
     }
-    // final update: the update list's wide matrices, then its tall ones
-    const int32_t* mat = lists + 2 * (2 * n_mats + 1);
-    const int32_t* begin = mat + n_mats;
-    for (int tall = 0; tall <= 1; ++tall)
-      for (int64_t it = 0; it < n_mats; ++it)
-        if (p.geom[mat[it]].tall == (tall == 1))
-          for (int32_t t = 0; t < begin[it + 1] - begin[it]; ++t) *tab++ = make_int2(mat[it], t);
   }
 
   hipError_t e = hipMemcpyAsync(ws, blob.data(), p.blob_bytes, hipMemcpyHostToDevice, stream);
