@@ -8,10 +8,20 @@ two device synchronizations.
 
 Prints one JSON line.  ``value`` is the Newton-Schulz algorithmic TFLOP/s of
 the whole step (NS flops per step / wall time per step); ``ms_per_step`` is
-the step time.  ``roofline`` describes the dominant kernel (most GPU time per
-step), timed with hipEvents recorded by the library around each of its
-launches on the launch stream inside the timed region.  ``cpu_baseline`` is
-the float64 oracle on a bounded sample of the same workload on the host cores.
+the step time.  The timed region runs the library exactly as a caller would
+(its Newton-Schulz stream groups included) with no per-kernel instrumentation.
+
+``roofline`` describes the dominant kernel (most GPU time per step).  It comes
+from a second pass of the same K steps right after the timed region, with the
+Newton-Schulz work on ONE stream (MFSDP_NS_GROUPS=1) so that no two kernels of
+the library overlap; the library records hipEvents around each of its launches
+on the launch stream, and ``achieved`` is the kernel's algorithmic flops (or
+bytes) per launch over its average launch duration.  ``kernels`` holds the
+same per-kind figures.  ``traffic`` is the kernel's measured HBM bytes per
+launch (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy) read from
+profiles/, or null when the kernel sources changed since it was measured.
+``cpu_baseline`` is the float64 oracle on a bounded sample of the same
+workload on the host cores.
 """
 
 from __future__ import annotations
@@ -109,7 +119,11 @@ def main():
                     help="before the run, copy this many MiB device-to-device with a plain "
                          "copy kernel (reference point for HBM byte counters)")
     ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+                    help="JSON file with measured HBM bytes per launch of the dominant kernel "
+                         "(default: profiles/<kernel>_<workload>_traffic.json)")
+    ap.add_argument("--ns-groups", type=int, default=0,
+                    help="Newton-Schulz stream groups in the timed region (0: the library's "
+                         "own choice)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -118,6 +132,7 @@ def main():
         sys.exit(2)
 
     import matrix_optimizer_step_owner_amd as mf
+    from matrix_optimizer_step_owner_amd import profiling
     from matrix_optimizer_step_owner_amd import workloads as wlm
 
     dev = torch.device("cuda:0")
@@ -147,20 +162,32 @@ def main():
                       beta2=wl.adam_beta2, eps=wl.adam_eps,
                       weight_decay=wl.adam_weight_decay, step=wl.adam_step)
 
+    if args.ns_groups > 0:
+        os.environ["MFSDP_NS_GROUPS"] = str(args.ns_groups)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    mf.timing.reset()
-    mf.timing.enable(True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    mf.timing.enable(False)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # roofline pass: the same steps with the Newton-Schulz work on one stream
+    saved = os.environ.get("MFSDP_NS_GROUPS")
+    os.environ["MFSDP_NS_GROUPS"] = "1"
+    mf.timing.reset()
+    mf.timing.enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    mf.timing.enable(False)
+    if saved is None:
+        del os.environ["MFSDP_NS_GROUPS"]
+    else:
+        os.environ["MFSDP_NS_GROUPS"] = saved
     per_kind = {}
     for k in KINDS:
         tot, cnt = mf.timing.read(k)
@@ -184,11 +211,17 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
     roof["kernel"] = dominant
+    roof["launches_per_step"] = per_kind[dominant]["launches"] // args.steps
+    roof["avg_launch_ms"] = round(per_kind[dominant]["avg_ms"], 5)
+    roof["pass"] = "one stream, the K steps after the timed region"
     roof["traffic"] = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
+    tpath = args.traffic or os.path.join(ROOT, "profiles",
+                                         f"{dominant}_kernel_{args.workload}_traffic.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
             tr = json.load(f)
-        if tr.get("kernel") == dominant and tr.get("workload") == args.workload:
+        if (tr.get("kernel") == dominant and tr.get("workload") == args.workload
+                and tr.get("source_sha256") == profiling.kernel_source_hash()):
             roof["traffic"] = tr.get("bytes_per_launch")
 
     kernels = {}
@@ -213,6 +246,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
+        "ns_groups": int(os.environ.get("MFSDP_NS_GROUPS", "0")) or "library",
         "config": {"workload": args.workload, "matrices": len(shapes),
                    "elements": wl.n_elements, "tail": wl.tail_n, "ns_steps": wl.ns_steps,
                    "ns_flops_per_step": ns_flops_step},

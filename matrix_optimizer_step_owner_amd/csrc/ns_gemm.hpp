@@ -162,7 +162,7 @@ __device__ __forceinline__ void apply8_vec(const MatDesc& d, size_t off, const R
 
 // Same for `cnt` (< 8 or unaligned) elements, one at a time.
 template <class E>
-__device__ __noinline__ void apply8_scalar(const MatDesc& d, size_t off, int cnt,
+__device__ __forceinline__ void apply8_scalar(const MatDesc& d, size_t off, int cnt,
                                               const float (&o)[8], float decay) {
   using S = typename E::storage_t;
   S* W = static_cast<S*>(d.W);
@@ -193,13 +193,16 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, const voi
   const uint32_t hi =
       static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
   const uint64_t ub = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds), "v"(voff), "s"(ub) : "memory", "m0");
+  // One wait state between the SALU write of M0 and the LDS DMA that reads it
+  // (a GFX9 hazard that the hardware does not interlock).
+  const uint32_t ulds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(ulds), "v"(voff), "s"(ub) : "memory", "m0");
 }
 
+// LDS byte address of a __shared__ object (a link-time constant).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((MFSDP_LDS const void*)p)));
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((MFSDP_LDS const void*)p));
 }
 
 // XOR swizzle of the 16-byte chunks of a K-contiguous LDS panel row (64 bytes).
@@ -207,6 +210,29 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // rows per bank row; a fragment read touches 16 consecutive rows at one
 // chunk, which (row >> 2) & 3 spreads over all 16 bank groups.
 __device__ __forceinline__ int kswz(int row) { return (row >> 2) & 3; }
+
+// Which DMA piece (0..7, or -1 for none) a K step issues in MFMA slot idx of
+// sub-step sub: the eight 1 KB pieces of a stage are spread over the step so
+// that the vector-memory queue never holds up the MFMA issue for long.
+#ifndef MFSDP_DMA_SCHED
+#define MFSDP_DMA_SCHED 0
+#endif
+__host__ __device__ constexpr int dma_slot_piece(int sub, int idx) {
+#if MFSDP_DMA_SCHED == 0
+  return (sub == 0 && idx < 8) ? idx : -1;
+#elif MFSDP_DMA_SCHED == 1
+  return (sub == 0 && (idx & 1) == 0) ? idx / 2 : -1;
+#else
+  return (idx & 3) == 0 ? 4 * sub + idx / 4 : -1;
+#endif
+}
+// DMAs that may stay in flight at the barrier of step t: those of step t - 1
+// and the ones step t issued before its barrier (step t + 1's must be done).
+#if MFSDP_DMA_SCHED == 2
+#define MFSDP_VM_IN_FLIGHT "12"
+#else
+#define MFSDP_VM_IN_FLIGHT "16"
+#endif
 
 template <class E, int MODE>
 __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
@@ -290,7 +316,12 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
       doff[q] = static_cast<uint32_t>((static_cast<size_t>(kk) * ldq + col0 + c * V) * sizeof(S));
     }
   }
-  auto dma_piece = [&](uint4* buf, int k0, int q) {
+  // Every DMA destination is a link-time constant (the stage object and the
+  // piece) plus this wave's uniform offset: no per-lane address work.
+  const uint32_t wave_off = static_cast<uint32_t>(wave) * 4096u;
+  auto dma_piece = [&](auto stage_c, int k0, int q) {
+    constexpr int stage = decltype(stage_c)::value;
+    const uint4* sbuf = stage == 0 ? st0 : stage == 1 ? st1 : stage == 2 ? st2 : st3;
     const char* base;
     if (q < 4)
       base = reinterpret_cast<const char*>(P + k0);
@@ -298,8 +329,9 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
       base = reinterpret_cast<const char*>(Q + k0);
     else
       base = reinterpret_cast<const char*>(Q + static_cast<size_t>(k0) * ldq);
-    uint4* dst = buf + (q < 4 ? 0 : PANEL) + wave * 256 + (q & 3) * 64;
-    lds_dma16(lds_addr(dst), doff[q], base);
+    const uint32_t dst = lds_addr(sbuf) + wave_off + (q < 4 ? 0u : PANEL * 16u) +
+                         static_cast<uint32_t>(q & 3) * 1024u;
+    lds_dma16(dst, doff[q], base);
   };
 
   // ---- fragments --------------------------------------------------------------
@@ -370,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   // MFMAs overlap the fragment reads of step t + 1 from stage N.
   // The barrier also orders every wave's last reads of stage Y (issued before
   // the previous barrier) before the DMA into Y.
-  auto kstep = [&](const uint4* X, uint4* Y, const uint4* N, int k_dma, auto dma_c,
+  auto kstep = [&](const uint4* X, auto Y, const uint4* N, int k_dma, auto dma_c,
                    auto next_c, auto wait_all_c) {
     constexpr bool do_dma = decltype(dma_c)::value;
     constexpr bool has_next = decltype(next_c)::value;
@@ -380,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
       Mma<E>::run(acc[idx >> 2][idx & 3], fa[0][idx >> 2], fb[0][idx & 3]);
       if (idx < kReadPieces) read_piece(X, 1, idx, fa[1], fb[1]);
       if constexpr (do_dma) {
-        if (idx < 8) dma_piece(Y, k_dma, idx);
+        if (dma_slot_piece(0, idx) >= 0) dma_piece(Y, k_dma, dma_slot_piece(0, idx));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -390,12 +422,15 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     if constexpr (wait_all)
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
-      asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(" MFSDP_VM_IN_FLIGHT ") lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
       Mma<E>::run(acc[idx >> 2][idx & 3], fa[1][idx >> 2], fb[1][idx & 3]);
       if constexpr (has_next) {
         if (idx < kReadPieces) read_piece(N, 0, idx, fa[0], fb[0]);
+      }
+      if constexpr (do_dma) {
+        if (dma_slot_piece(1, idx) >= 0) dma_piece(Y, k_dma, dma_slot_piece(1, idx));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -404,29 +439,33 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   // ---- main loop: four stages, unrolled by four ----------------------------
   using yes = std::integral_constant<bool, true>;
   using no = std::integral_constant<bool, false>;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
   const int nk = K / BK;                // multiple of 8: K is a multiple of 256
   // prologue: steps 0..2 in flight, wait for step 0
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dma_piece(st0, 0, q);
+  for (int q = 0; q < 8; ++q) dma_piece(S0{}, 0, q);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dma_piece(st1, BK, q);
+  for (int q = 0; q < 8; ++q) dma_piece(S1{}, BK, q);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dma_piece(st2, 2 * BK, q);
+  for (int q = 0; q < 8; ++q) dma_piece(S2{}, 2 * BK, q);
   asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int p = 0; p < kReadPieces; ++p) read_piece(st0, 0, p, fa[0], fb[0]);
   int t = 0;
   for (; t + 8 <= nk; t += 4) {
-    kstep(st0, st3, st1, (t + 3) * BK, yes{}, yes{}, no{});
-    kstep(st1, st0, st2, (t + 4) * BK, yes{}, yes{}, no{});
-    kstep(st2, st1, st3, (t + 5) * BK, yes{}, yes{}, no{});
-    kstep(st3, st2, st0, (t + 6) * BK, yes{}, yes{}, no{});
+    kstep(st0, S3{}, st1, (t + 3) * BK, yes{}, yes{}, no{});
+    kstep(st1, S0{}, st2, (t + 4) * BK, yes{}, yes{}, no{});
+    kstep(st2, S1{}, st3, (t + 5) * BK, yes{}, yes{}, no{});
+    kstep(st3, S2{}, st0, (t + 6) * BK, yes{}, yes{}, no{});
   }
   // last four steps: only the first still has a step (nk - 1) to prefetch
-  kstep(st0, st3, st1, (t + 3) * BK, yes{}, yes{}, yes{});
-  kstep(st1, st0, st2, 0, no{}, yes{}, yes{});
-  kstep(st2, st1, st3, 0, no{}, yes{}, yes{});
-  kstep(st3, st2, st0, 0, no{}, no{}, yes{});
+  kstep(st0, S3{}, st1, (t + 3) * BK, yes{}, yes{}, yes{});
+  kstep(st1, S0{}, st2, 0, no{}, yes{}, yes{});
+  kstep(st2, S1{}, st3, 0, no{}, yes{}, yes{});
+  kstep(st3, S2{}, st0, 0, no{}, no{}, yes{});
   __syncthreads();
 
   // ---- epilogue through LDS -------------------------------------------------
@@ -473,10 +512,24 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
 
   // One 64 x 256 block per accumulator row i; i is a compile-time constant
   // so that acc stays in registers.
+  // pass B coordinates of iteration p: eight consecutive tile rows of one
+  // tile column
+  auto coordB = [&](int i, int p, int& gcol, int& grow0, int& sl, int& sub, int& c_in) {
+    const int it = p * kThreads + tid;
+    const int tc = it >> 3, q = it & 7;
+    const int wrr = q >> 2, wcc = tc >> 7;
+    sub = q & 3;
+    c_in = tc & 127;
+    sl = wrr * 2 + wcc;
+    grow0 = row0 + wrr * 128 + i * 32 + sub * 8;
+    gcol = col0 + tc;
+  };
+
   auto block = [&](auto i_c) {
     constexpr int i = decltype(i_c)::value;
-    // global inputs of pass A, issued before the staging so that their
-    // latency overlaps it
+    // global inputs of both passes, issued before the staging so that their
+    // latency overlaps it (the weights: pass A for a wide apply, pass B for
+    // a tall one)
     Raw8 xin[8], win[8];
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
@@ -485,6 +538,12 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
       if (MODE != kModeGram) xin[p] = load_raw8<E>(ein + static_cast<size_t>(grow) * ldo + gcol);
       if (wide_apply && vec && grow < d.m && gcol + 8 <= d.n)
         win[p] = load_raw8<E>(W + static_cast<size_t>(grow) * d.cols + gcol);
+      if constexpr (tall_apply) {
+        int bcol, brow0, bsl, bsub, bc_in;
+        coordB(i, p, bcol, brow0, bsl, bsub, bc_in);
+        if (vec && bcol < d.n && brow0 + 8 <= d.m)
+          win[p] = load_raw8<E>(W + static_cast<size_t>(bcol) * d.cols + brow0);
+      }
     }
     {
       float* reg = slice_of(wave);
@@ -540,29 +599,10 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     // Pass B: column-wise, eight consecutive tile rows of one tile column.
     if (mirror || tall_apply) {
       __syncthreads();
-      auto coordB = [&](int p, int& gcol, int& grow0, int& sl, int& sub, int& c_in) {
-        const int it = p * kThreads + tid;
-        const int tc = it >> 3, q = it & 7;
-        const int wrr = q >> 2, wcc = tc >> 7;
-        sub = q & 3;
-        c_in = tc & 127;
-        sl = wrr * 2 + wcc;
-        grow0 = row0 + wrr * 128 + i * 32 + sub * 8;
-        gcol = col0 + tc;
-      };
-      if constexpr (tall_apply) {
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          int gcol, grow0, sl, sub, c_in;
-          coordB(p, gcol, grow0, sl, sub, c_in);
-          if (vec && gcol < d.n && grow0 + 8 <= d.m)
-            win[p] = load_raw8<E>(W + static_cast<size_t>(gcol) * d.cols + grow0);
-        }
-      }
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         int gcol, grow0, sl, sub, c_in;
-        coordB(p, gcol, grow0, sl, sub, c_in);
+        coordB(i, p, gcol, grow0, sl, sub, c_in);
         const float* slice = slice_of(sl);
         float v[8];
 #pragma unroll

@@ -1,0 +1,154 @@
+"""Text summaries of rocprofv3 output for the library's kernels.
+
+Two inputs are understood:
+
+* ``--kernel-trace --stats -f csv`` output (``*_kernel_stats.csv``): per kernel
+  calls, average and total duration;
+* ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` runs (``*_counter_collection.csv``,
+  one run per counter): HBM bytes per dispatch.  Both counters are in KiB per
+  dispatch; each is divided by what the same counter reads, per byte, for a
+  plain device-to-device copy of known size recorded in the same run (the
+  largest ``copyBuffer`` dispatch), which calibrates it to bytes.
+
+Usage (after copying the rocprofv3 output back):
+
+  python -m matrix_optimizer_step_owner_amd.profiling stats KT_kernel_stats.csv \
+      --command "<the profiled command>" --out profiles/<kernels>_<workload>.txt
+  python -m matrix_optimizer_step_owner_amd.profiling traffic FETCH.csv WRITE.csv \
+      --calib-mib 1024 --kernel update --workload block_d2048 \
+      --command "<the profiled command>" --out profiles/update_kernel_block_d2048_traffic.json
+"""
+
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+from typing import Dict, List
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+
+_NS_MODES = {"0": "gram", "1": "poly", "2": "update", "3": "final_wide", "4": "final_tall"}
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources of the library (identifies a kernel build)."""
+    d = os.path.join(PKG_DIR, "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def short_name(kernel: str) -> str:
+    """Library kernel kind of a demangled kernel name ('' for other kernels)."""
+    m = re.search(r"ns_gemm_kernel<mfsdp::Elem(BF16|F32), (\d)>", kernel)
+    if m:
+        return _NS_MODES[m.group(2)] + ("" if m.group(1) == "BF16" else "_f32")
+    for key, name in (("momentum_kernel", "momentum"), ("norm_finalize_kernel", "norm"),
+                      ("adamw_kernel", "adamw"), ("apply_x0_kernel", "apply")):
+        if key in kernel:
+            return name
+    return ""
+
+
+def kernel_stats(stats_csv: str) -> List[dict]:
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append({"kernel": r["Name"], "kind": short_name(r["Name"]),
+                         "calls": int(r["Calls"]),
+                         "avg_us": float(r["AverageNs"]) / 1e3,
+                         "min_us": float(r["MinNs"]) / 1e3,
+                         "max_us": float(r["MaxNs"]) / 1e3,
+                         "total_ms": float(r["TotalDurationNs"]) / 1e6,
+                         "pct": float(r["Percentage"])})
+    return rows
+
+
+def format_stats(rows: List[dict], command: str) -> str:
+    out = ["rocprofv3 --kernel-trace --stats summary", "", "command:", "  " + command, "",
+           f"{'kind':12s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s} "
+           f"{'total ms':>10s} {'%':>6s}  kernel"]
+    for r in rows:
+        out.append(f"{r['kind'] or '-':12s} {r['calls']:6d} {r['avg_us']:10.2f} {r['min_us']:10.2f} "
+                   f"{r['max_us']:10.2f} {r['total_ms']:10.3f} {r['pct']:6.2f}  {r['kernel'][:90]}")
+    return "\n".join(out) + "\n"
+
+
+def counter_by_dispatch(pmc_csv: str, counter: str) -> List[dict]:
+    """Per dispatch: kernel name and the counter summed over its rows."""
+    acc: Dict[int, dict] = collections.OrderedDict()
+    with open(pmc_csv) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = acc.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"], "value": 0.0})
+            d["value"] += float(r["Counter_Value"])
+    return list(acc.values())
+
+
+def traffic(fetch_csv: str, write_csv: str, calib_bytes: int, kind: str) -> dict:
+    """Calibrated HBM bytes per launch of kernel kind ``kind``."""
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        ds = counter_by_dispatch(path, counter)
+        copies = [d["value"] for d in ds if "copyBuffer" in d["kernel"]]
+        if not copies:
+            raise SystemExit(f"{path}: no copy dispatch to calibrate {counter}")
+        factor = max(copies) * 1024.0 / calib_bytes
+        vals = [d["value"] * 1024.0 / factor for d in ds if short_name(d["kernel"]) == kind]
+        if not vals:
+            raise SystemExit(f"{path}: no dispatch of kernel kind {kind!r}")
+        res[counter] = {"factor": factor, "dispatches": len(vals),
+                        "bytes_per_launch": sum(vals) / len(vals)}
+    return res
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser(prog="python -m matrix_optimizer_step_owner_amd.profiling")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("stats_csv")
+    s.add_argument("--command", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_csv")
+    t.add_argument("write_csv")
+    t.add_argument("--calib-mib", type=int, required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        text = format_stats(kernel_stats(a.stats_csv), a.command)
+        with open(a.out, "w") as f:
+            f.write(text)
+        print(text)
+    else:
+        tr = traffic(a.fetch_csv, a.write_csv, a.calib_mib << 20, a.kernel)
+        doc = {"kernel": a.kernel, "workload": a.workload,
+               "bytes_per_launch": tr["FETCH_SIZE"]["bytes_per_launch"]
+               + tr["WRITE_SIZE"]["bytes_per_launch"],
+               "fetch_bytes_per_launch": tr["FETCH_SIZE"]["bytes_per_launch"],
+               "write_bytes_per_launch": tr["WRITE_SIZE"]["bytes_per_launch"],
+               "fetch_calibration_factor": tr["FETCH_SIZE"]["factor"],
+               "write_calibration_factor": tr["WRITE_SIZE"]["factor"],
+               "dispatches": tr["FETCH_SIZE"]["dispatches"],
+               "source_sha256": kernel_source_hash(),
+               "command": a.command}
+        with open(a.out, "w") as f:
+            json.dump(doc, f, indent=1)
+            f.write("\n")
+        print(json.dumps(doc, indent=1))
+
+
+if __name__ == "__main__":
+    main()
