@@ -246,6 +246,20 @@ def random_tail_state(n: int, seed: int, p_std: float = 0.02,
             torch.from_numpy(v))
 
 
+def trajectory_gradients(shapes, dtype: torch.dtype, steps: int, seed: int,
+                         g_std: float = 1e-3, tail_n: int = 0, tail_g_std: float = 1e-3):
+    """Per-step gradients of a multi-step run: step t draws, from
+    ``default_rng([seed, t])``, one G per shape (listing order) and then the
+    tail gradient.  Returns ``[(Gs, tail_g), ...]`` with one entry per step."""
+    out = []
+    for t in range(steps):
+        rng = np.random.default_rng([seed, t])
+        Gs = [_to_storage(_normal(rng, tuple(s), g_std), dtype) for s in shapes]
+        g = torch.from_numpy(_normal(rng, (tail_n,), tail_g_std))
+        out.append((Gs, g))
+    return out
+
+
 def describe(key: str) -> str:
     wl = WORKLOADS[key]
     return (f"{wl.key}: {len(wl.matrices)} matrices, {wl.n_elements:,} "

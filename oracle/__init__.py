@@ -32,6 +32,9 @@ Parity status of each function (what pins it, see ``tests/test_oracle_pins.py``)
 * ``quintic_scalar_exact``   pinned (it is the scalar map the SVD closed form composes)
 * ``default_scale``          parity unpinned: the pages fix no update scale; the
                              value follows the common original-Muon convention.
+* ``round_to_bf16``          pinned (torch's float32 -> bfloat16 conversion, hand-worked ties)
+* ``muon_trajectory``        pinned (one step = the single-step oracle; momentum closed form)
+* ``adamw_trajectory``       pinned (constant-gradient closed form over many steps)
 """
 
 from .muon_ref import (
@@ -45,16 +48,21 @@ from .muon_ref import (
 )
 from .adamw_ref import adamw_tail
 from .ns_scalar import quintic_scalar_exact, quintic_scalar_float
+from .trajectory import adamw_trajectory, muon_trajectory, round_to_bf16, round_to_f32
 
 __all__ = [
     "NS_EPS",
     "adamw_tail",
+    "adamw_trajectory",
     "default_scale",
     "frobenius_normalize",
     "momentum_nesterov",
     "muon_matrix_step",
     "muon_step",
+    "muon_trajectory",
     "newton_schulz",
     "quintic_scalar_exact",
     "quintic_scalar_float",
+    "round_to_bf16",
+    "round_to_f32",
 ]
