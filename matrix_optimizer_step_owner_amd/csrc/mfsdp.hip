@@ -154,7 +154,6 @@ int choose_groups(int64_t n, int64_t upd_total) {
   const int64_t rounds = upd_total / kCus;
   if (upd_total < kCus / 4) g = 1;          // latency-bound; not worth streams
   else if (rounds >= 6) g = 1;
-  else if (rounds >= 2) g = 2;
   else g = 3;
   if (const char* env = getenv("MFSDP_NS_GROUPS")) {
     const int v = atoi(env);

@@ -538,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
       if (MODE != kModeGram) xin[p] = load_raw8<E>(ein + static_cast<size_t>(grow) * ldo + gcol);
       if (wide_apply && vec && grow < d.m && gcol + 8 <= d.n)
         win[p] = load_raw8<E>(W + static_cast<size_t>(grow) * d.cols + gcol);
-      if constexpr (tall_apply) {
+      if constexpr (tall_apply && V == 8) {   // fp32: loaded in pass B (registers)
         int bcol, brow0, bsl, bsub, bc_in;
         coordB(i, p, bcol, brow0, bsl, bsub, bc_in);
         if (vec && bcol < d.n && brow0 + 8 <= d.m)
@@ -611,10 +611,14 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
           store8<E>(out + static_cast<size_t>(gcol) * ldo + grow0, v);
         } else if (tall_apply && gcol < d.n && grow0 < d.m) {
           const size_t uo = static_cast<size_t>(gcol) * d.cols + grow0;
-          if (vec && grow0 + 8 <= d.m)
-            apply8_vec<E>(d, uo, win[p], v, ep.decay);
-          else
+          if (vec && grow0 + 8 <= d.m) {
+            if constexpr (V == 8)
+              apply8_vec<E>(d, uo, win[p], v, ep.decay);
+            else
+              apply8_vec<E>(d, uo, load_raw8<E>(W + uo), v, ep.decay);
+          } else {
             apply8_scalar<E>(d, uo, min(8, d.m - grow0), v, ep.decay);
+          }
         }
       }
     }
