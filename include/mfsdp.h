@@ -150,6 +150,82 @@ mfsdp_status_t mfsdp_adamw_tail(float* param, const float* grad,
                                 float weight_decay, int64_t step,
                                 hipStream_t stream);
 
+/*
+ * Balance-aware owner planner (host only; touches no device).
+ *
+ * Source: arxivlens page, Summary (a balance-aware owner planner assigns
+ * ownership by bytes and by work); gist.science summaries, "Méthodologie",
+ * part 2, first mechanism (a global planner chooses owners so that resident
+ * bytes and optimizer work are balanced across the ranks).  The pages give no
+ * algorithm; this one is greedy longest-processing-time-first scheduling
+ * (Graham 1969) under a per-owner byte cap.
+ *
+ * Items are whole: a 2D matrix or a tail tensor, each going to exactly one of
+ * n_ranks owners.
+ *   cost_ms[n_items]   host, predicted optimizer-step time of each item on its
+ *                      owner (for example measured per shape); finite, >= 0
+ *   bytes[n_items]     host, resident bytes of each item on its owner (weight,
+ *                      gradient and optimizer state); >= 0
+ *   byte_slack         each owner's bytes stay within
+ *                      cap = ceil((1 + byte_slack) * max(total/n_ranks, largest))
+ *                      when any owner can take the item under it
+ * In order of decreasing cost (ties: more bytes first, then lower index), each
+ * item goes to the owner with the least predicted time among those it keeps
+ * under the cap (ties: lower rank); when none can, to the owner with the
+ * fewest bytes.  Without a binding cap the largest predicted time is within
+ * (4/3 - 1/(3 n_ranks)) of the optimum.  Deterministic.
+ * Outputs (host): owner[n_items] in [0, n_ranks); rank_ms[n_ranks] = summed
+ * cost per owner; rank_bytes[n_ranks] = summed bytes per owner.
+ * Errors: MFSDP_ERR_INVALID_ARGUMENT (n_items < 0, n_ranks < 1, null
+ * pointers, negative or non-finite cost, negative bytes or slack).
+ */
+mfsdp_status_t mfsdp_plan_owners(const double* cost_ms, const int64_t* bytes,
+                                 int64_t n_items, int32_t n_ranks,
+                                 double byte_slack, int32_t* owner,
+                                 double* rank_ms, int64_t* rank_bytes);
+
+/*
+ * Packed tail layout (host only).  Source: arxivlens Abstract and gist.science
+ * "Méthodologie", part 1: non-matrix tensors are packed into a tail owner,
+ * which runs AdamW on the packed buffer.
+ * Tensor i of numel[i] fp32 elements occupies elements
+ * [offsets[i], offsets[i] + numel[i]) of the packed buffer; segments follow
+ * in order, each starting on a 16-byte (4-element) boundary.  *total is the
+ * packed length (the last segment rounded up to 4).
+ * Errors: MFSDP_ERR_INVALID_ARGUMENT (n < 0, null pointers, numel < 0).
+ */
+mfsdp_status_t mfsdp_tail_layout(const int64_t* numel, int64_t n,
+                                 int64_t* offsets, int64_t* total);
+
+/*
+ * Gather tensors into a packed fp32 tail (device copy on `stream`).
+ *   src[n]      host array of device pointers, tensor i of numel[i] fp32
+ *               elements (4-byte aligned; may be NULL when numel[i] == 0)
+ *   offsets[n]  host, element offsets in the packed buffer: multiples of 4,
+ *               segments [offset, offset + round_up(numel, 4)) in bounds and
+ *               pairwise disjoint (mfsdp_tail_layout gives such offsets)
+ *   packed      device, packed_numel fp32 elements, 16-byte aligned; must not
+ *               overlap any source
+ * Each segment receives its tensor followed by zeros up to the next 4-element
+ * boundary; elements outside every segment are left unchanged.
+ * Errors: MFSDP_ERR_INVALID_ARGUMENT, MFSDP_ERR_ALIAS (overlapping segments,
+ * or a source overlapping the packed buffer), MFSDP_ERR_HIP.
+ */
+mfsdp_status_t mfsdp_tail_pack(const float* const* src, const int64_t* numel,
+                               const int64_t* offsets, int64_t n, float* packed,
+                               int64_t packed_numel, hipStream_t stream);
+
+/*
+ * Scatter a packed fp32 tail back into its tensors (device copy on `stream`):
+ * dst[i][0 .. numel[i]) = packed[offsets[i] ..].  Same argument rules as
+ * mfsdp_tail_pack; the destinations must not overlap each other or the
+ * packed buffer (MFSDP_ERR_ALIAS).
+ */
+mfsdp_status_t mfsdp_tail_unpack(const float* packed, int64_t packed_numel,
+                                 float* const* dst, const int64_t* numel,
+                                 const int64_t* offsets, int64_t n,
+                                 hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* mfsdp_status_string(mfsdp_status_t status);
 

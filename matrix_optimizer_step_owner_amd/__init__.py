@@ -24,6 +24,7 @@ from . import _lib
 from ._lib import MfsdpError, NS_EPS
 
 __all__ = ["muon_step", "adamw_tail", "muon_workspace_size", "default_scale",
+           "plan_owners", "tail_layout", "tail_pack", "tail_unpack",
            "timing", "MfsdpError", "NS_EPS", "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -174,6 +175,91 @@ def adamw_tail(p: torch.Tensor, g: torch.Tensor, m: torch.Tensor, v: torch.Tenso
     _lib.check(lib.mfsdp_adamw_tail(p.data_ptr(), g.data_ptr(), m.data_ptr(),
                                     v.data_ptr(), n, lr, beta1, beta2, eps,
                                     weight_decay, step, stream))
+
+
+def plan_owners(cost_ms: Sequence[float], nbytes: Sequence[int], n_ranks: int,
+                byte_slack: float = 0.1):
+    """Balance-aware owner assignment of whole items (mfsdp_plan_owners).
+
+    Returns (owner per item, predicted ms per rank, resident bytes per rank).
+    Host only.
+    """
+    lib = _lib.load()
+    n = len(cost_ms)
+    if len(nbytes) != n:
+        raise ValueError("cost_ms and nbytes must have the same length")
+    c = (ctypes.c_double * max(n, 1))(*[float(x) for x in cost_ms])
+    b = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in nbytes])
+    owner = (ctypes.c_int32 * max(n, 1))()
+    rms = (ctypes.c_double * max(n_ranks, 1))()
+    rbytes = (ctypes.c_int64 * max(n_ranks, 1))()
+    _lib.check(lib.mfsdp_plan_owners(c, b, n, n_ranks, byte_slack, owner, rms, rbytes))
+    return ([int(owner[i]) for i in range(n)], [float(rms[r]) for r in range(n_ranks)],
+            [int(rbytes[r]) for r in range(n_ranks)])
+
+
+def tail_layout(numels: Sequence[int]):
+    """Offsets of tensors packed in order into one fp32 tail, each segment on a
+    16-byte boundary (mfsdp_tail_layout).  Returns (offsets, total)."""
+    lib = _lib.load()
+    n = len(numels)
+    arr = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in numels])
+    off = (ctypes.c_int64 * max(n, 1))()
+    total = ctypes.c_int64(0)
+    _lib.check(lib.mfsdp_tail_layout(arr, n, off, ctypes.byref(total)))
+    return [int(off[i]) for i in range(n)], int(total.value)
+
+
+def _tail_args(tensors, offsets):
+    n = len(tensors)
+    if len(offsets) != n:
+        raise ValueError("one offset per tensor")
+    ptrs = (ctypes.c_void_p * max(n, 1))()
+    nums = (ctypes.c_int64 * max(n, 1))()
+    offs = (ctypes.c_int64 * max(n, 1))(*[int(o) for o in offsets])
+    for i, t in enumerate(tensors):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"tail tensor {i} must be a contiguous fp32 tensor")
+        ptrs[i] = t.data_ptr() if t.numel() else None
+        nums[i] = t.numel()
+    return ptrs, nums, offs
+
+
+def tail_pack(tensors: Sequence[torch.Tensor], packed: Optional[torch.Tensor] = None,
+              offsets: Optional[Sequence[int]] = None):
+    """Gather fp32 tensors (any shape, contiguous) into a packed tail
+    (mfsdp_tail_pack).  Returns (packed, offsets)."""
+    lib = _lib.load()
+    if offsets is None:
+        offsets, total = tail_layout([t.numel() for t in tensors])
+    else:
+        total = max([o + (t.numel() + 3) // 4 * 4 for o, t in zip(offsets, tensors)] or [0])
+    if packed is None:
+        device = tensors[0].device if tensors else torch.device("cuda")
+        packed = torch.empty(total, dtype=torch.float32, device=device)
+    if packed.dtype != torch.float32 or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous fp32 tensor")
+    if len(tensors) == 0:
+        return packed, list(offsets)
+    ptrs, nums, offs = _tail_args(tensors, offsets)
+    stream = torch.cuda.current_stream(packed.device).cuda_stream
+    _lib.check(lib.mfsdp_tail_pack(ptrs, nums, offs, len(tensors), packed.data_ptr(),
+                                   packed.numel(), stream))
+    return packed, list(offsets)
+
+
+def tail_unpack(packed: torch.Tensor, tensors: Sequence[torch.Tensor],
+                offsets: Sequence[int]) -> None:
+    """Scatter a packed fp32 tail back into its tensors (mfsdp_tail_unpack)."""
+    lib = _lib.load()
+    if len(tensors) == 0:
+        return
+    if packed.dtype != torch.float32 or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous fp32 tensor")
+    ptrs, nums, offs = _tail_args(tensors, offsets)
+    stream = torch.cuda.current_stream(packed.device).cuda_stream
+    _lib.check(lib.mfsdp_tail_unpack(packed.data_ptr(), packed.numel(), ptrs, nums, offs,
+                                     len(tensors), stream))
 
 
 class timing:

@@ -21,8 +21,9 @@ KERNEL_KINDS = {"momentum": 0, "norm": 1, "gram": 2, "poly": 3, "update": 4,
 
 #: Every symbol include/mfsdp.h declares.
 EXPORTED = ("mfsdp_muon_workspace_size", "mfsdp_muon_step", "mfsdp_adamw_tail",
-            "mfsdp_status_string", "mfsdp_last_error", "mfsdp_timing_enable",
-            "mfsdp_timing_reset", "mfsdp_timing_read")
+            "mfsdp_plan_owners", "mfsdp_tail_layout", "mfsdp_tail_pack",
+            "mfsdp_tail_unpack", "mfsdp_status_string", "mfsdp_last_error",
+            "mfsdp_timing_enable", "mfsdp_timing_reset", "mfsdp_timing_read")
 
 
 class MfsdpMatrix(ctypes.Structure):
@@ -72,6 +73,21 @@ def load() -> ctypes.CDLL:
             c.c_float, c.c_float, c.c_float, c.c_float, c.c_float, c.c_int64,
             c.c_void_p]
         lib.mfsdp_adamw_tail.restype = c.c_int
+        lib.mfsdp_plan_owners.argtypes = [
+            c.POINTER(c.c_double), c.POINTER(c.c_int64), c.c_int64, c.c_int32, c.c_double,
+            c.POINTER(c.c_int32), c.POINTER(c.c_double), c.POINTER(c.c_int64)]
+        lib.mfsdp_plan_owners.restype = c.c_int
+        lib.mfsdp_tail_layout.argtypes = [c.POINTER(c.c_int64), c.c_int64,
+                                          c.POINTER(c.c_int64), c.POINTER(c.c_int64)]
+        lib.mfsdp_tail_layout.restype = c.c_int
+        lib.mfsdp_tail_pack.argtypes = [
+            c.POINTER(c.c_void_p), c.POINTER(c.c_int64), c.POINTER(c.c_int64), c.c_int64,
+            c.c_void_p, c.c_int64, c.c_void_p]
+        lib.mfsdp_tail_pack.restype = c.c_int
+        lib.mfsdp_tail_unpack.argtypes = [
+            c.c_void_p, c.c_int64, c.POINTER(c.c_void_p), c.POINTER(c.c_int64),
+            c.POINTER(c.c_int64), c.c_int64, c.c_void_p]
+        lib.mfsdp_tail_unpack.restype = c.c_int
         lib.mfsdp_status_string.argtypes = [c.c_int]
         lib.mfsdp_status_string.restype = c.c_char_p
         lib.mfsdp_last_error.argtypes = []

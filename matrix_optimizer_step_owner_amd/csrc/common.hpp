@@ -70,6 +70,12 @@ __device__ __forceinline__ void gst<uint4>(void* p, const uint4& v) {
 }
 
 template <>
+__device__ __forceinline__ float4 gld<float4>(const void* p) {
+  const f32x4_t v = *(const MFSDP_GLOBAL f32x4_t*)(p);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+template <>
 __device__ __forceinline__ void gst<float4>(void* p, const float4& v) {
   *(MFSDP_GLOBAL f32x4_t*)(p) = f32x4_t{v.x, v.y, v.z, v.w};
 }

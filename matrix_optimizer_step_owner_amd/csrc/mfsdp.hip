@@ -24,6 +24,8 @@
 #include "common.hpp"
 #include "ew_kernels.hpp"
 #include "ns_gemm.hpp"
+#include "planner.hpp"
+#include "tail_kernels.hpp"
 
 namespace {
 
@@ -710,6 +712,175 @@ mfsdp_status_t mfsdp_adamw_tail(float* param, const float* grad, float* exp_avg,
   try {
     return adamw_tail_impl(param, grad, exp_avg, exp_avg_sq, n, lr, beta1, beta2, eps,
                            weight_decay, step, stream);
+  } catch (const std::exception& ex) {
+    return fail(MFSDP_ERR_UNSUPPORTED, "host exception: %s", ex.what());
+  }
+}
+
+mfsdp_status_t mfsdp_plan_owners(const double* cost_ms, const int64_t* bytes, int64_t n_items,
+                                 int32_t n_ranks, double byte_slack, int32_t* owner,
+                                 double* rank_ms, int64_t* rank_bytes) {
+  try {
+    g_last_error.clear();
+    if (n_items < 0 || n_ranks < 1)
+      return fail(MFSDP_ERR_INVALID_ARGUMENT, "n_items=%lld n_ranks=%d", (long long)n_items,
+                  n_ranks);
+    if (!rank_ms || !rank_bytes || (n_items > 0 && (!cost_ms || !bytes || !owner)))
+      return fail(MFSDP_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!(byte_slack >= 0.0) || !std::isfinite(byte_slack))
+      return fail(MFSDP_ERR_INVALID_ARGUMENT, "byte_slack must be finite and >= 0");
+    for (int64_t i = 0; i < n_items; ++i) {
+      if (!(cost_ms[i] >= 0.0) || !std::isfinite(cost_ms[i]))
+        return fail(MFSDP_ERR_INVALID_ARGUMENT, "item %lld: cost must be finite and >= 0",
+                    (long long)i);
+      if (bytes[i] < 0)
+        return fail(MFSDP_ERR_INVALID_ARGUMENT, "item %lld: bytes < 0", (long long)i);
+    }
+    plan_lpt(cost_ms, bytes, n_items, n_ranks, byte_slack, owner, rank_ms, rank_bytes);
+    return MFSDP_OK;
+  } catch (const std::exception& ex) {
+    return fail(MFSDP_ERR_UNSUPPORTED, "host exception: %s", ex.what());
+  }
+}
+
+mfsdp_status_t mfsdp_tail_layout(const int64_t* numel, int64_t n, int64_t* offsets,
+                                 int64_t* total) {
+  g_last_error.clear();
+  if (n < 0 || !total || (n > 0 && (!numel || !offsets)))
+    return fail(MFSDP_ERR_INVALID_ARGUMENT, "bad tail layout arguments");
+  for (int64_t i = 0; i < n; ++i)
+    if (numel[i] < 0) return fail(MFSDP_ERR_INVALID_ARGUMENT, "tensor %lld: numel < 0",
+                                  (long long)i);
+  *total = tail_layout(numel, n, offsets);
+  return MFSDP_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared by pack (to_packed) and unpack: validate, then copy in launches of
+// up to kTailSegs segments.
+mfsdp_status_t tail_copy(float* packed_rw, int64_t packed_numel, float* const* tensors,
+                         const int64_t* numel, const int64_t* offsets, int64_t n, bool to_packed,
+                         hipStream_t stream) {
+  g_last_error.clear();
+  if (n < 0 || packed_numel < 0)
+    return fail(MFSDP_ERR_INVALID_ARGUMENT, "n=%lld packed_numel=%lld", (long long)n,
+                (long long)packed_numel);
+  if (n == 0) return MFSDP_OK;
+  if (!numel || !offsets || !tensors || !packed_rw)
+    return fail(MFSDP_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(packed_rw, 16))
+    return fail(MFSDP_ERR_INVALID_ARGUMENT, "packed buffer must be 16-byte aligned");
+  std::vector<int64_t> order(n);
+  for (int64_t i = 0; i < n; ++i) {
+    if (numel[i] < 0 || offsets[i] < 0 || offsets[i] % kTailAlign != 0)
+      return fail(MFSDP_ERR_INVALID_ARGUMENT,
+                  "tensor %lld: numel >= 0 and a non-negative offset multiple of %lld needed",
+                  (long long)i, (long long)kTailAlign);
+    const int64_t span = (numel[i] + kTailAlign - 1) / kTailAlign * kTailAlign;
+    if (offsets[i] + span > packed_numel)
+      return fail(MFSDP_ERR_INVALID_ARGUMENT, "tensor %lld: segment ends past the buffer",
+                  (long long)i);
+    if (numel[i] > 0 && !tensors[i])
+      return fail(MFSDP_ERR_INVALID_ARGUMENT, "tensor %lld: null pointer", (long long)i);
+    if (numel[i] > 0 && (reinterpret_cast<uintptr_t>(tensors[i]) & 3) != 0)
+      return fail(MFSDP_ERR_INVALID_ARGUMENT, "tensor %lld: not 4-byte aligned", (long long)i);
+    order[i] = i;
+  }
+  // empty segments occupy nothing and are left out of the overlap check
+  order.erase(std::remove_if(order.begin(), order.end(),
+                             [&](int64_t i) { return numel[i] == 0; }),
+              order.end());
+  std::sort(order.begin(), order.end(),
+            [&](int64_t a, int64_t b) { return offsets[a] < offsets[b]; });
+  for (size_t j = 1; j < order.size(); ++j) {
+    const int64_t a = order[j - 1], b = order[j];
+    const int64_t span_a = (numel[a] + kTailAlign - 1) / kTailAlign * kTailAlign;
+    if (offsets[a] + span_a > offsets[b])
+      return fail(MFSDP_ERR_ALIAS, "segments of tensors %lld and %lld overlap", (long long)a,
+                  (long long)b);
+  }
+  // tensors must not overlap the packed buffer
+  {
+    std::vector<Range> rs;
+    rs.push_back({reinterpret_cast<uintptr_t>(packed_rw),
+                  reinterpret_cast<uintptr_t>(packed_rw + packed_numel), "packed buffer", -1});
+    for (int64_t i = 0; i < n; ++i)
+      if (numel[i] > 0)
+        rs.push_back({reinterpret_cast<uintptr_t>(tensors[i]),
+                      reinterpret_cast<uintptr_t>(tensors[i] + numel[i]), "tensor", i});
+    if (!to_packed) {   // unpack writes every tensor: they must not overlap each other either
+      mfsdp_status_t st = check_aliasing(rs);
+      if (st != MFSDP_OK) return st;
+    } else {
+      const uintptr_t lo = rs[0].lo, hi = rs[0].hi;
+      for (size_t k = 1; k < rs.size(); ++k)
+        if (rs[k].lo < hi && lo < rs[k].hi)
+          return fail(MFSDP_ERR_ALIAS, "tensor %lld overlaps the packed buffer",
+                      (long long)rs[k].idx);
+    }
+  }
+  TailBatch b{};
+  auto flush = [&]() -> hipError_t {
+    if (b.count == 0) return hipSuccess;
+    const int64_t blocks = b.block0[b.count];
+    hipError_t e = hipSuccess;
+    if (blocks > 0) {
+      tail_copy_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream>>>(b);
+      e = hipGetLastError();
+    }
+    b = TailBatch{};
+    return e;
+  };
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t span = to_packed ? (numel[i] + kTailAlign - 1) / kTailAlign * kTailAlign
+                                   : numel[i];
+    if (span == 0) continue;
+    TailSeg& g = b.seg[b.count];
+    if (to_packed) {
+      g.src = tensors[i];
+      g.dst = packed_rw + offsets[i];
+    } else {
+      g.src = packed_rw + offsets[i];
+      g.dst = tensors[i];
+    }
+    g.n = numel[i];
+    g.span = span;
+    b.block0[b.count + 1] = b.block0[b.count] + (span + kTailBlockElems - 1) / kTailBlockElems;
+    ++b.count;
+    if (b.count == kTailSegs || b.block0[b.count] > (int64_t(1) << 30)) {
+      hipError_t e = flush();
+      if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "tail copy: %s", hipGetErrorString(e));
+    }
+  }
+  hipError_t e = flush();
+  if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "tail copy: %s", hipGetErrorString(e));
+  return MFSDP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mfsdp_status_t mfsdp_tail_pack(const float* const* src, const int64_t* numel,
+                               const int64_t* offsets, int64_t n, float* packed,
+                               int64_t packed_numel, hipStream_t stream) {
+  try {
+    return tail_copy(packed, packed_numel, const_cast<float* const*>(src), numel, offsets, n,
+                     true, stream);
+  } catch (const std::exception& ex) {
+    return fail(MFSDP_ERR_UNSUPPORTED, "host exception: %s", ex.what());
+  }
+}
+
+mfsdp_status_t mfsdp_tail_unpack(const float* packed, int64_t packed_numel, float* const* dst,
+                                 const int64_t* numel, const int64_t* offsets, int64_t n,
+                                 hipStream_t stream) {
+  try {
+    return tail_copy(const_cast<float*>(packed), packed_numel, dst, numel, offsets, n, false,
+                     stream);
   } catch (const std::exception& ex) {
     return fail(MFSDP_ERR_UNSUPPORTED, "host exception: %s", ex.what());
   }

@@ -35,6 +35,9 @@ Parity status of each function (what pins it, see ``tests/test_oracle_pins.py``)
 * ``round_to_bf16``          pinned (torch's float32 -> bfloat16 conversion, hand-worked ties)
 * ``muon_trajectory``        pinned (one step = the single-step oracle; momentum closed form)
 * ``adamw_trajectory``       pinned (constant-gradient closed form over many steps)
+* ``planner_ref``            the LPT rule pinned by a hand-worked schedule and Graham's
+                             4/3 - 1/(3R) bound against brute-force optima; the
+                             tail layout by hand-worked offsets
 """
 
 from .muon_ref import (
@@ -49,6 +52,7 @@ from .muon_ref import (
 from .adamw_ref import adamw_tail
 from .ns_scalar import quintic_scalar_exact, quintic_scalar_float
 from .trajectory import adamw_trajectory, muon_trajectory, round_to_bf16, round_to_f32
+from . import planner_ref
 
 __all__ = [
     "NS_EPS",
@@ -61,6 +65,7 @@ __all__ = [
     "muon_step",
     "muon_trajectory",
     "newton_schulz",
+    "planner_ref",
     "quintic_scalar_exact",
     "quintic_scalar_float",
     "round_to_bf16",
