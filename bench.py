@@ -107,6 +107,56 @@ def cpu_baseline(key, budget_s=20.0):
                       f"{done_flops:.3e}"}
 
 
+def stats_bench(args, wl, dev):
+    """Time mfsdp_shampoo_stats over the workload's gradients (one line of JSON).
+
+    Algorithmic work: the symmetric products counted once, r(r+1)c flops for L
+    and c(c+1)r for R per r x c gradient.  The dominant kernel is the
+    statistics product (kind "syrk"); its roofline is the dtype's MFMA peak.
+    """
+    import matrix_optimizer_step_owner_amd as mf
+    from matrix_optimizer_step_owner_amd import workloads as wlm
+    inp = wlm.generate(args.workload, seed=0)
+    G = [t.to(dev) for t in inp.grads]
+    del inp
+    L = [torch.zeros(g.shape[0], g.shape[0], device=dev) for g in G]
+    R = [torch.zeros(g.shape[1], g.shape[1], device=dev) for g in G]
+    flops = sum(r * (r + 1) * c + c * (c + 1) * r for r, c in (g.shape for g in G))
+    hp = dict(beta=0.95, alpha=0.05)
+    for _ in range(args.warmup):
+        mf.shampoo_stats(G, L, R, **hp)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        mf.shampoo_stats(G, L, R, **hp)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    mf.timing.reset()
+    mf.timing.enable(True)
+    for _ in range(args.steps):
+        mf.shampoo_stats(G, L, R, **hp)
+    torch.cuda.synchronize()
+    mf.timing.enable(False)
+    kern = {}
+    for k in ("stats_prep", "syrk"):
+        tot, cnt = mf.timing.read(k)
+        if cnt:
+            kern[k] = {"avg_ms": round(tot / cnt, 5)}
+    peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_FP32_MFMA_TFLOPS
+    ach = flops / (kern["syrk"]["avg_ms"] * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "Shampoo-type statistics update L,R (TFLOP/s, symmetric products once)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "matrices": len(G), "flops_per_step": flops},
+        "kernels": kern,
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                     "frac": ach / peak, "kernel": "syrk", "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +171,9 @@ def main():
     ap.add_argument("--traffic", default=None,
                     help="JSON file with measured HBM bytes per launch of the dominant kernel "
                          "(default: profiles/<kernel>_<workload>_traffic.json)")
+    ap.add_argument("--shampoo-stats", action="store_true",
+                    help="measure the Shampoo-type statistics update (L += G G^T, "
+                         "R += G^T G) on the workload's gradients instead of the Muon step")
     ap.add_argument("--ns-groups", type=int, default=0,
                     help="Newton-Schulz stream groups in the timed region (0: the library's "
                          "own choice)")
@@ -144,6 +197,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     wl = wlm.WORKLOADS[args.workload]
+    if args.shampoo_stats:
+        stats_bench(args, wl, dev)
+        return
     inp = wlm.generate(args.workload, seed=0)
     shapes = [(s.rows, s.cols) for s in wl.matrices]
     W = [t.to(dev) for t in inp.weights]

@@ -226,6 +226,50 @@ mfsdp_status_t mfsdp_tail_unpack(const float* packed, int64_t packed_numel,
                                  const int64_t* offsets, int64_t n,
                                  hipStream_t stream);
 
+/*
+ * Preconditioner statistics of Shampoo-type matrix optimizers on the owner.
+ *
+ * Source: arxivlens page, Abstract and Key takeaways, and gist.science
+ * summaries, "Contributions clés": the owner-shaped layout serves matrix
+ * optimizers in general (Shampoo and SOAP as well as Muon), since each needs
+ * the whole 2D gradient on one rank.  The pages give no formulas; the
+ * statistics are the textbook Shampoo ones (Gupta, Koren and Singer 2018),
+ * with SOAP's exponential moving average as the beta/alpha form.
+ *
+ * One whole gradient of the list, row-major rows x cols in the call's dtype:
+ *   grad    device, read only
+ *   left    device fp32 rows x rows, updated in place:  L <- beta*L + alpha*G G^T
+ *   right   device fp32 cols x cols or NULL, updated:   R <- beta*R + alpha*G^T G
+ * The products accumulate in fp32 from the stored gradient values (bf16 or
+ * fp32); L and R stay exactly symmetric (the upper triangle is computed and
+ * mirrored).  beta == 0 overwrites L and R without reading them.
+ */
+typedef struct mfsdp_stats_matrix {
+  const void* grad;
+  float* left;
+  float* right;
+  int64_t rows;
+  int64_t cols;
+} mfsdp_stats_matrix_t;
+
+/* Workspace bytes for mfsdp_shampoo_stats (host only): two zero-padded copies
+ * of each gradient (G and its transpose, 256-padded) and launch tables.
+ * n_mats == 0 gives 0.  Errors: MFSDP_ERR_INVALID_ARGUMENT, MFSDP_ERR_UNSUPPORTED
+ * (dtype, or a size beyond the 32-bit offsets of the kernels). */
+mfsdp_status_t mfsdp_stats_workspace_size(const mfsdp_stats_matrix_t* mats,
+                                          int64_t n_mats, mfsdp_dtype_t dtype,
+                                          size_t* out_bytes);
+
+/* Statistics update over the list, enqueued on `stream`.  workspace: device,
+ * >= mfsdp_stats_workspace_size bytes, 256-byte aligned, scratch.
+ * Validation before any launch: rows, cols >= 1; non-null grad and left;
+ * naturally aligned buffers; grad/left/right/workspace pairwise disjoint
+ * across the list (MFSDP_ERR_ALIAS); finite beta and alpha. */
+mfsdp_status_t mfsdp_shampoo_stats(const mfsdp_stats_matrix_t* mats, int64_t n_mats,
+                                   mfsdp_dtype_t dtype, float beta, float alpha,
+                                   void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* mfsdp_status_string(mfsdp_status_t status);
 
@@ -250,7 +294,9 @@ typedef enum mfsdp_kernel_kind {
   MFSDP_KERNEL_APPLY = 5,     /* apply when ns_steps == 0            */
   MFSDP_KERNEL_ADAMW = 6,     /* AdamW tail                          */
   MFSDP_KERNEL_FINAL = 7,     /* last update, applies W (2 launches) */
-  MFSDP_KERNEL_KINDS = 8
+  MFSDP_KERNEL_STATS_PREP = 8,/* gradient copies for the statistics   */
+  MFSDP_KERNEL_SYRK = 9,      /* L, R statistics products            */
+  MFSDP_KERNEL_KINDS = 10
 } mfsdp_kernel_kind_t;
 
 mfsdp_status_t mfsdp_timing_enable(int enable);

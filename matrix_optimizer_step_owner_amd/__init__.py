@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import MfsdpError, NS_EPS
 
 __all__ = ["muon_step", "adamw_tail", "muon_workspace_size", "default_scale",
-           "plan_owners", "tail_layout", "tail_pack", "tail_unpack",
+           "plan_owners", "tail_layout", "tail_pack", "tail_unpack", "shampoo_stats",
            "timing", "MfsdpError", "NS_EPS", "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -175,6 +175,53 @@ def adamw_tail(p: torch.Tensor, g: torch.Tensor, m: torch.Tensor, v: torch.Tenso
     _lib.check(lib.mfsdp_adamw_tail(p.data_ptr(), g.data_ptr(), m.data_ptr(),
                                     v.data_ptr(), n, lr, beta1, beta2, eps,
                                     weight_decay, step, stream))
+
+
+def shampoo_stats(grads: Sequence[torch.Tensor], lefts: Sequence[torch.Tensor],
+                  rights: Optional[Sequence[Optional[torch.Tensor]]] = None, *,
+                  beta: float = 1.0, alpha: float = 1.0,
+                  workspace: Optional[torch.Tensor] = None) -> None:
+    """Preconditioner statistics in place (mfsdp_shampoo_stats):
+    L <- beta*L + alpha*G G^T and, where given, R <- beta*R + alpha*G^T G.
+
+    grads: 2D contiguous bf16 or fp32 tensors on one GPU; lefts / rights:
+    contiguous fp32 (rows x rows) / (cols x cols).  Runs on torch's current
+    stream."""
+    lib = _lib.load()
+    n = len(grads)
+    if len(lefts) != n or (rights is not None and len(rights) != n):
+        raise ValueError("one left (and right) statistic per gradient")
+    if n == 0:
+        return
+    dtype = grads[0].dtype
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    device = grads[0].device
+    if device.type != "cuda":
+        raise ValueError("shampoo_stats needs GPU tensors")
+    arr = (_lib.MfsdpStatsMatrix * n)()
+    for i, G in enumerate(grads):
+        if G.dim() != 2:
+            raise ValueError(f"grads[{i}] must be 2D")
+        r, c = G.shape
+        _check_matrix(G, f"grads[{i}]", dtype, device)
+        _check_matrix(lefts[i], f"lefts[{i}]", torch.float32, device, (r, r))
+        R = None if rights is None else rights[i]
+        if R is not None:
+            _check_matrix(R, f"rights[{i}]", torch.float32, device, (c, c))
+        arr[i].grad = G.data_ptr()
+        arr[i].left = lefts[i].data_ptr()
+        arr[i].right = None if R is None else R.data_ptr()
+        arr[i].rows = r
+        arr[i].cols = c
+    code = _DTYPES[dtype]
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.mfsdp_stats_workspace_size(arr, n, code, ctypes.byref(need)))
+    stream = torch.cuda.current_stream(device).cuda_stream
+    if workspace is None:
+        workspace = _workspace(device, stream, need.value)
+    _lib.check(lib.mfsdp_shampoo_stats(arr, n, code, beta, alpha, workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), stream))
 
 
 def plan_owners(cost_ms: Sequence[float], nbytes: Sequence[int], n_ranks: int,

@@ -17,12 +17,13 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 NS_EPS = 1e-7
 KERNEL_KINDS = {"momentum": 0, "norm": 1, "gram": 2, "poly": 3, "update": 4,
-                "apply": 5, "adamw": 6, "final": 7}
+                "apply": 5, "adamw": 6, "final": 7, "stats_prep": 8, "syrk": 9}
 
 #: Every symbol include/mfsdp.h declares.
 EXPORTED = ("mfsdp_muon_workspace_size", "mfsdp_muon_step", "mfsdp_adamw_tail",
             "mfsdp_plan_owners", "mfsdp_tail_layout", "mfsdp_tail_pack",
-            "mfsdp_tail_unpack", "mfsdp_status_string", "mfsdp_last_error",
+            "mfsdp_tail_unpack", "mfsdp_stats_workspace_size", "mfsdp_shampoo_stats",
+            "mfsdp_status_string", "mfsdp_last_error",
             "mfsdp_timing_enable", "mfsdp_timing_reset", "mfsdp_timing_read")
 
 
@@ -34,6 +35,14 @@ class MfsdpMatrix(ctypes.Structure):
                 ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64),
                 ("scale", ctypes.c_float)]
+
+
+class MfsdpStatsMatrix(ctypes.Structure):
+    _fields_ = [("grad", ctypes.c_void_p),
+                ("left", ctypes.c_void_p),
+                ("right", ctypes.c_void_p),
+                ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64)]
 
 
 class MfsdpError(RuntimeError):
@@ -88,6 +97,13 @@ def load() -> ctypes.CDLL:
             c.c_void_p, c.c_int64, c.POINTER(c.c_void_p), c.POINTER(c.c_int64),
             c.POINTER(c.c_int64), c.c_int64, c.c_void_p]
         lib.mfsdp_tail_unpack.restype = c.c_int
+        lib.mfsdp_stats_workspace_size.argtypes = [
+            c.POINTER(MfsdpStatsMatrix), c.c_int64, c.c_int, c.POINTER(c.c_size_t)]
+        lib.mfsdp_stats_workspace_size.restype = c.c_int
+        lib.mfsdp_shampoo_stats.argtypes = [
+            c.POINTER(MfsdpStatsMatrix), c.c_int64, c.c_int, c.c_float, c.c_float,
+            c.c_void_p, c.c_size_t, c.c_void_p]
+        lib.mfsdp_shampoo_stats.restype = c.c_int
         lib.mfsdp_status_string.argtypes = [c.c_int]
         lib.mfsdp_status_string.restype = c.c_char_p
         lib.mfsdp_last_error.argtypes = []

@@ -25,6 +25,7 @@
 #include "ew_kernels.hpp"
 #include "ns_gemm.hpp"
 #include "planner.hpp"
+#include "stats_kernels.hpp"
 #include "tail_kernels.hpp"
 
 namespace {
@@ -164,7 +165,7 @@ int choose_groups(int64_t n, int64_t upd_total) {
   return static_cast<int>(std::min<int64_t>(g, n));
 }
 
-mfsdp_status_t make_geom(const mfsdp_matrix_t& mt, int64_t idx, MatGeom* g) {
+mfsdp_status_t make_geom(const mfsdp_matrix_t& mt, int64_t idx, MatGeom* g, size_t es) {
   if (mt.rows < 1 || mt.cols < 1)
     return fail(MFSDP_ERR_INVALID_ARGUMENT, "matrix %lld: rows=%lld cols=%lld must be >= 1",
                 (long long)idx, (long long)mt.rows, (long long)mt.cols);
@@ -175,9 +176,12 @@ mfsdp_status_t make_geom(const mfsdp_matrix_t& mt, int64_t idx, MatGeom* g) {
   g->n = std::max(mt.rows, mt.cols);
   g->m_pad = round_up(g->m, kTile);
   g->n_pad = round_up(g->n, kTile);
-  if (g->n_pad > (int64_t(1) << 24) || g->m_pad * g->n_pad >= (int64_t(1) << 31))
+  // Kernels address an iterate with 32-bit byte offsets from its base.
+  if (g->n_pad > (int64_t(1) << 24) || g->m_pad * g->n_pad >= (int64_t(1) << 31) ||
+      g->m_pad * g->n_pad * static_cast<int64_t>(es) >= (int64_t(1) << 32))
     return fail(MFSDP_ERR_UNSUPPORTED,
-                "matrix %lld: %lld x %lld exceeds the 2^31-element iterate limit",
+                "matrix %lld: %lld x %lld exceeds the iterate size limit (2^31 elements, "
+                "2^32 bytes)",
                 (long long)idx, (long long)mt.rows, (long long)mt.cols);
   g->ew_tiles_j = g->n_pad / kEwTile;
   g->ew_ntiles = (g->m_pad / kEwTile) * g->ew_tiles_j;
@@ -188,7 +192,7 @@ mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t d
   const size_t es = elem_size(dt);
   p->geom.resize(n);
   for (int64_t i = 0; i < n; ++i) {
-    mfsdp_status_t st = make_geom(mats[i], i, &p->geom[i]);
+    mfsdp_status_t st = make_geom(mats[i], i, &p->geom[i], es);
     if (st != MFSDP_OK) return st;
     p->ew_total += p->geom[i].ew_ntiles;
     const int64_t tm = p->geom[i].m_pad / kTile, tn = p->geom[i].n_pad / kTile;
@@ -441,9 +445,224 @@ hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nest
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// Preconditioner statistics (Shampoo-type): L <- beta*L + alpha*G G^T,
+// R <- beta*R + alpha*G^T G for each gradient of the list.
+// ---------------------------------------------------------------------------
+struct StatsPlan {
+  std::vector<int64_t> r_pad, c_pad;
+  std::vector<size_t> off_xg, off_xt;
+  int64_t prep_tiles = 0, syrk_tiles = 0, n_syrk = 0;
+  size_t off_prep = 0, off_syrk = 0, off_lists = 0, off_tiles = 0, off_scales = 0;
+  size_t blob_bytes = 0, total = 0;
+};
+
+mfsdp_status_t build_stats_plan(const mfsdp_stats_matrix_t* mats, int64_t n, size_t es,
+                                StatsPlan* p) {
+  p->r_pad.resize(n);
+  p->c_pad.resize(n);
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t r = mats[i].rows, c = mats[i].cols;
+    if (r < 1 || c < 1)
+      return fail(MFSDP_ERR_INVALID_ARGUMENT, "matrix %lld: rows=%lld cols=%lld must be >= 1",
+                  (long long)i, (long long)r, (long long)c);
+    const int64_t rp = round_up(r, kTile), cp = round_up(c, kTile);
+    if (rp > (int64_t(1) << 24) || cp > (int64_t(1) << 24) || rp * cp >= (int64_t(1) << 31) ||
+        rp * cp * static_cast<int64_t>(es) >= (int64_t(1) << 32) ||
+        std::max(r, c) * std::max(r, c) >= (int64_t(1) << 31))
+      return fail(MFSDP_ERR_UNSUPPORTED, "matrix %lld: %lld x %lld exceeds the size limit",
+                  (long long)i, (long long)r, (long long)c);
+    p->r_pad[i] = rp;
+    p->c_pad[i] = cp;
+    p->prep_tiles += (rp / kEwTile) * (cp / kEwTile);
+    const int64_t tr = rp / kTile, tc = cp / kTile;
+    p->syrk_tiles += tr * (tr + 1) / 2;
+    p->n_syrk += 1;
+    if (mats[i].right) {
+      p->syrk_tiles += tc * (tc + 1) / 2;
+      p->n_syrk += 1;
+    }
+  }
+  if (p->prep_tiles >= (int64_t(1) << 31) || p->syrk_tiles >= (int64_t(1) << 31))
+    return fail(MFSDP_ERR_UNSUPPORTED, "too many tiles in one call");
+  size_t off = 0;
+  p->off_prep = off;
+  off = align_up(off + n * sizeof(MatDesc), kWsAlign);
+  p->off_syrk = off;
+  off = align_up(off + p->n_syrk * sizeof(MatDesc), kWsAlign);
+  p->off_lists = off;
+  off = align_up(off + (2 * n + 1) * sizeof(int32_t), kWsAlign);
+  p->off_tiles = off;
+  off = align_up(off + p->syrk_tiles * sizeof(int2), kWsAlign);
+  p->off_scales = off;
+  off = align_up(off + p->n_syrk * sizeof(float), kWsAlign);
+  p->blob_bytes = off;
+  p->off_xg.resize(n);
+  p->off_xt.resize(n);
+  for (int64_t i = 0; i < n; ++i) {
+    const size_t xb = size_t(p->r_pad[i]) * size_t(p->c_pad[i]) * es;
+    p->off_xg[i] = off; off = align_up(off + xb, kWsAlign);
+    p->off_xt[i] = off; off = align_up(off + xb, kWsAlign);
+  }
+  p->total = off;
+  return MFSDP_OK;
+}
+
+mfsdp_status_t stats_validate(const mfsdp_stats_matrix_t* mats, int64_t n, mfsdp_dtype_t dtype) {
+  if (n < 0) return fail(MFSDP_ERR_INVALID_ARGUMENT, "n_mats < 0");
+  if (n > 0 && !mats) return fail(MFSDP_ERR_INVALID_ARGUMENT, "mats is NULL");
+  if (dtype != MFSDP_DTYPE_F32 && dtype != MFSDP_DTYPE_BF16)
+    return fail(MFSDP_ERR_UNSUPPORTED, "dtype %d", static_cast<int>(dtype));
+  if (n > (int64_t(1) << 24)) return fail(MFSDP_ERR_UNSUPPORTED, "too many matrices");
+  return MFSDP_OK;
+}
+
+template <class E>
+hipError_t enqueue_stats(const StatsPlan& p, int64_t n, char* ws, float alpha, float beta,
+                         hipStream_t stream) {
+  const MatDesc* prep = reinterpret_cast<const MatDesc*>(ws + p.off_prep);
+  const MatDesc* syrk = reinterpret_cast<const MatDesc*>(ws + p.off_syrk);
+  const int32_t* lists = reinterpret_cast<const int32_t*>(ws + p.off_lists);
+  WorkList wl;
+  wl.mat = lists;
+  wl.begin = lists + n;
+  wl.n_items = static_cast<int32_t>(n);
+  hipError_t e = launch(MFSDP_KERNEL_STATS_PREP, stream, [&] {
+    stats_prep_kernel<E><<<dim3(static_cast<unsigned>(p.prep_tiles)), dim3(kThreads), 0,
+                           stream>>>(prep, wl);
+  });
+  if (e != hipSuccess) return e;
+  NsEpi ep{};
+  ep.cur = 0;
+  ep.a = alpha;
+  ep.b = beta;
+  return launch(MFSDP_KERNEL_SYRK, stream, [&] {
+    ns_gemm_kernel<E, kModeSyrk><<<dim3(static_cast<unsigned>(p.syrk_tiles)), dim3(kThreads), 0,
+                                   stream>>>(syrk, reinterpret_cast<const int2*>(ws + p.off_tiles),
+                                             reinterpret_cast<const float*>(ws + p.off_scales),
+                                             ep);
+  });
+}
+
+mfsdp_status_t stats_impl(const mfsdp_stats_matrix_t* mats, int64_t n, mfsdp_dtype_t dtype,
+                          float beta, float alpha, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  g_last_error.clear();
+  mfsdp_status_t st = stats_validate(mats, n, dtype);
+  if (st != MFSDP_OK) return st;
+  if (!std::isfinite(beta) || !std::isfinite(alpha))
+    return fail(MFSDP_ERR_INVALID_ARGUMENT, "beta and alpha must be finite");
+  if (n == 0) return MFSDP_OK;
+  const size_t es = elem_size(dtype);
+  StatsPlan p;
+  st = build_stats_plan(mats, n, es, &p);
+  if (st != MFSDP_OK) return st;
+  if (!workspace || workspace_bytes < p.total)
+    return fail(MFSDP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                p.total);
+  if (!aligned(workspace, kWsAlign))
+    return fail(MFSDP_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kWsAlign);
+  std::vector<Range> rs;
+  rs.push_back({reinterpret_cast<uintptr_t>(workspace),
+                reinterpret_cast<uintptr_t>(workspace) + p.total, "workspace", -1});
+  for (int64_t i = 0; i < n; ++i) {
+    const mfsdp_stats_matrix_t& m = mats[i];
+    if (!m.grad || !m.left)
+      return fail(MFSDP_ERR_INVALID_ARGUMENT, "matrix %lld: grad and left are required",
+                  (long long)i);
+    if (!aligned(m.grad, es) || !aligned(m.left, 4) || (m.right && !aligned(m.right, 4)))
+      return fail(MFSDP_ERR_INVALID_ARGUMENT, "matrix %lld: misaligned buffer", (long long)i);
+    const uintptr_t g = reinterpret_cast<uintptr_t>(m.grad);
+    const uintptr_t l = reinterpret_cast<uintptr_t>(m.left);
+    rs.push_back({g, g + size_t(m.rows) * size_t(m.cols) * es, "grad", i});
+    rs.push_back({l, l + size_t(m.rows) * size_t(m.rows) * 4, "left", i});
+    if (m.right) {
+      const uintptr_t r = reinterpret_cast<uintptr_t>(m.right);
+      rs.push_back({r, r + size_t(m.cols) * size_t(m.cols) * 4, "right", i});
+    }
+  }
+  st = check_aliasing(rs);
+  if (st != MFSDP_OK) return st;
+
+  char* ws = static_cast<char*>(workspace);
+  std::vector<char> blob(p.blob_bytes, 0);
+  MatDesc* prep = reinterpret_cast<MatDesc*>(blob.data() + p.off_prep);
+  MatDesc* syrk = reinterpret_cast<MatDesc*>(blob.data() + p.off_syrk);
+  int32_t* lists = reinterpret_cast<int32_t*>(blob.data() + p.off_lists);
+  int2* tab = reinterpret_cast<int2*>(blob.data() + p.off_tiles);
+  int64_t acc = 0, k = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const mfsdp_stats_matrix_t& m = mats[i];
+    MatDesc& d = prep[i];
+    d.G = m.grad;
+    d.X0 = ws + p.off_xg[i];
+    d.X1 = ws + p.off_xt[i];
+    d.rows = static_cast<int32_t>(m.rows);
+    d.cols = static_cast<int32_t>(m.cols);
+    d.m_pad = static_cast<int32_t>(p.r_pad[i]);
+    d.n_pad = static_cast<int32_t>(p.c_pad[i]);
+    d.ew_tiles_j = static_cast<int32_t>(p.c_pad[i] / kEwTile);
+    lists[i] = static_cast<int32_t>(i);
+    lists[n + i] = static_cast<int32_t>(acc);
+    acc += (p.r_pad[i] / kEwTile) * (p.c_pad[i] / kEwTile);
+    // L = Xg Xg^T (valid rows x rows); R = Xt Xt^T (valid cols x cols)
+    for (int side = 0; side < 2; ++side) {
+      if (side == 1 && !m.right) continue;
+      MatDesc& s = syrk[k];
+      s.X0 = side == 0 ? d.X0 : d.X1;
+      s.A = side == 0 ? static_cast<void*>(m.left) : static_cast<void*>(m.right);
+      s.m = static_cast<int32_t>(side == 0 ? m.rows : m.cols);
+      s.m_pad = static_cast<int32_t>(side == 0 ? p.r_pad[i] : p.c_pad[i]);
+      s.n_pad = static_cast<int32_t>(side == 0 ? p.c_pad[i] : p.r_pad[i]);
+      const int64_t tm = s.m_pad / kTile;
+      for (int64_t q = 0; q < tm * (tm + 1) / 2; ++q)
+        *tab++ = make_int2(static_cast<int>(k), static_cast<int>(q));
+      ++k;
+    }
+  }
+  lists[2 * n] = static_cast<int32_t>(acc);
+  hipError_t e = hipMemcpyAsync(ws, blob.data(), p.blob_bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "descriptor upload: %s", hipGetErrorString(e));
+  e = dtype == MFSDP_DTYPE_BF16 ? enqueue_stats<ElemBF16>(p, n, ws, alpha, beta, stream)
+                                : enqueue_stats<ElemF32>(p, n, ws, alpha, beta, stream);
+  if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "launch: %s", hipGetErrorString(e));
+  return MFSDP_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+mfsdp_status_t mfsdp_stats_workspace_size(const mfsdp_stats_matrix_t* mats, int64_t n_mats,
+                                          mfsdp_dtype_t dtype, size_t* out_bytes) {
+  try {
+    g_last_error.clear();
+    if (!out_bytes) return fail(MFSDP_ERR_INVALID_ARGUMENT, "out_bytes is NULL");
+    mfsdp_status_t st = stats_validate(mats, n_mats, dtype);
+    if (st != MFSDP_OK) return st;
+    if (n_mats == 0) {
+      *out_bytes = 0;
+      return MFSDP_OK;
+    }
+    StatsPlan p;
+    st = build_stats_plan(mats, n_mats, elem_size(dtype), &p);
+    if (st != MFSDP_OK) return st;
+    *out_bytes = p.total;
+    return MFSDP_OK;
+  } catch (const std::exception& ex) {
+    return fail(MFSDP_ERR_UNSUPPORTED, "host exception: %s", ex.what());
+  }
+}
+
+mfsdp_status_t mfsdp_shampoo_stats(const mfsdp_stats_matrix_t* mats, int64_t n_mats,
+                                   mfsdp_dtype_t dtype, float beta, float alpha,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    return stats_impl(mats, n_mats, dtype, beta, alpha, workspace, workspace_bytes, stream);
+  } catch (const std::exception& ex) {
+    return fail(MFSDP_ERR_UNSUPPORTED, "host exception: %s", ex.what());
+  }
+}
 
 const char* mfsdp_status_string(mfsdp_status_t s) {
   switch (s) {

@@ -30,13 +30,45 @@ namespace mfsdp {
 // wide (rows <= cols, row-major apply), kModeApplyTall for tall ones (the
 // transposed apply).  Separate kernels keep each one's code small: the
 // epilogue runs once per tile and is fetched into the instruction cache anew.
+// kModeSyrk is the Gram product of a padded gradient accumulated into a
+// caller's fp32 statistics matrix (Shampoo-type preconditioner statistics):
+// out <- b*out + a*X X^T over the valid m x m block (NsEpi a, b), the upper
+// tiles computed and mirrored.
 enum NsMode {
   kModeGram = 0,
   kModePoly = 1,
   kModeUpdate = 2,
   kModeApplyWide = 3,
-  kModeApplyTall = 4
+  kModeApplyTall = 4,
+  kModeSyrk = 5
 };
+
+// out <- beta*out + alpha*v for the elements of a row segment that lie inside
+// the valid m x m block (fp32, row pitch m).  beta == 0 ignores the old value.
+__device__ __forceinline__ void syrk_acc8(float* out, int m, int row, int col0,
+                                          const float (&v)[8], float alpha, float beta) {
+  if (row >= m) return;
+  float* q0 = out + static_cast<size_t>(row) * m + col0;
+  if (col0 + 8 <= m && ((reinterpret_cast<uintptr_t>(q0) & 15) == 0)) {
+    float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
+    if (beta != 0.f) {
+      lo = gld<float4>(q0);
+      hi = gld<float4>(q0 + 4);
+    }
+    gst<float4>(q0, make_float4(fmaf(beta, lo.x, alpha * v[0]), fmaf(beta, lo.y, alpha * v[1]),
+                                fmaf(beta, lo.z, alpha * v[2]), fmaf(beta, lo.w, alpha * v[3])));
+    gst<float4>(q0 + 4, make_float4(fmaf(beta, hi.x, alpha * v[4]), fmaf(beta, hi.y, alpha * v[5]),
+                                    fmaf(beta, hi.z, alpha * v[6]), fmaf(beta, hi.w, alpha * v[7])));
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (col0 + e < m) {
+      float* q = out + static_cast<size_t>(row) * m + col0 + e;
+      *q = beta == 0.f ? alpha * v[e] : fmaf(beta, *q, alpha * v[e]);
+    }
+  }
+}
 
 struct NsEpi {
   int cur;        // 0: the current iterate is X0, 1: X1
@@ -275,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   const S* P;
   const S* Q;
   int ldp, ldq, K;
-  if (MODE == kModeGram) {
+  if (MODE == kModeGram || MODE == kModeSyrk) {
     P = Xcur; Q = Xcur; ldp = ldq = d.n_pad; K = d.n_pad;
   } else if (MODE == kModePoly) {
     P = static_cast<const S*>(d.A); Q = P; ldp = ldq = d.m_pad; K = d.m_pad;
@@ -535,7 +567,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     for (int p = 0; p < 8; ++p) {
       int grow, gcol, sl, r_in, c_in;
       coordA(i, p, grow, gcol, sl, r_in, c_in);
-      if (MODE != kModeGram) xin[p] = load_raw8<E>(ein + static_cast<size_t>(grow) * ldo + gcol);
+      if (MODE != kModeGram && MODE != kModeSyrk)
+        xin[p] = load_raw8<E>(ein + static_cast<size_t>(grow) * ldo + gcol);
       if (wide_apply && vec && grow < d.m && gcol + 8 <= d.n)
         win[p] = load_raw8<E>(W + static_cast<size_t>(grow) * d.cols + gcol);
       if constexpr (tall_apply && V == 8) {   // fp32: loaded in pass B (registers)
@@ -570,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
       if (MODE == kModeGram) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= alpha;
-      } else {
+      } else if (MODE != kModeSyrk) {
         float x8[8];
         unpack_raw8<E>(xin[p], x8);
         if (MODE == kModePoly) {
@@ -581,7 +614,9 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
           for (int e = 0; e < 8; ++e) v[e] = alpha * fmaf(ep.kb, v[e], ep.a * x8[e]);
         }
       }
-      if constexpr (!kApply) {
+      if constexpr (MODE == kModeSyrk) {
+        syrk_acc8(static_cast<float*>(d.A), d.m, grow, gcol, v, ep.a, ep.b);
+      } else if constexpr (!kApply) {
         store8<E>(out + goff, v);
       } else if (wide_apply && grow < d.m && gcol < d.n) {
         const size_t uo = static_cast<size_t>(grow) * d.cols + gcol;
@@ -607,7 +642,9 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = slice[sidx(sub * 8 + e, c_in)];
-        if constexpr (sym) {
+        if constexpr (MODE == kModeSyrk) {
+          syrk_acc8(static_cast<float*>(d.A), d.m, gcol, grow0, v, ep.a, ep.b);
+        } else if constexpr (sym) {
           store8<E>(out + static_cast<size_t>(gcol) * ldo + grow0, v);
         } else if (tall_apply && gcol < d.n && grow0 < d.m) {
           const size_t uo = static_cast<size_t>(gcol) * d.cols + grow0;

@@ -35,6 +35,8 @@ Parity status of each function (what pins it, see ``tests/test_oracle_pins.py``)
 * ``round_to_bf16``          pinned (torch's float32 -> bfloat16 conversion, hand-worked ties)
 * ``muon_trajectory``        pinned (one step = the single-step oracle; momentum closed form)
 * ``adamw_trajectory``       pinned (constant-gradient closed form over many steps)
+* ``shampoo_stats``          pinned (Frobenius/trace identity, rank-1 closed form, shared
+                             nonzero spectrum of G G^T and G^T G, triple-loop definition)
 * ``planner_ref``            the LPT rule pinned by a hand-worked schedule and Graham's
                              4/3 - 1/(3R) bound against brute-force optima; the
                              tail layout by hand-worked offsets
@@ -53,6 +55,7 @@ from .adamw_ref import adamw_tail
 from .ns_scalar import quintic_scalar_exact, quintic_scalar_float
 from .trajectory import adamw_trajectory, muon_trajectory, round_to_bf16, round_to_f32
 from . import planner_ref
+from .shampoo_ref import shampoo_stats
 
 __all__ = [
     "NS_EPS",
@@ -70,4 +73,5 @@ __all__ = [
     "quintic_scalar_float",
     "round_to_bf16",
     "round_to_f32",
+    "shampoo_stats",
 ]

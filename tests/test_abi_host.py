@@ -207,3 +207,39 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         mf.adamw_tail(p, p.clone(), p.clone(), p.clone(), lr=0.1)
     mf.muon_step([], [], [], lr=0.1)   # non-owner: no-op
+
+
+def test_stats_workspace_and_validation():
+    lib = _lib.load()
+    M = _lib.MfsdpStatsMatrix
+    arr = (M * 2)()
+    arr[0].grad, arr[0].left, arr[0].right, arr[0].rows, arr[0].cols = 0x100000, 0x200000, 0x300000, 300, 1000
+    arr[1].grad, arr[1].left, arr[1].right, arr[1].rows, arr[1].cols = 0x400000, 0x500000, None, 17, 33
+    out = ctypes.c_size_t(0)
+    assert lib.mfsdp_stats_workspace_size(arr, 2, _lib.DTYPE_BF16, ctypes.byref(out)) == 0
+    # two padded copies per gradient: 512 x 1024 and 256 x 256, bf16
+    want = 2 * 2 * (512 * 1024 + 256 * 256)
+    assert want <= out.value <= want + (1 << 20)
+    assert lib.mfsdp_stats_workspace_size(arr, 0, _lib.DTYPE_BF16, ctypes.byref(out)) == 0
+    assert out.value == 0
+    # invalid calls return before any device work (fake addresses never used)
+    ws = 0x10000000
+    assert lib.mfsdp_shampoo_stats(arr, 2, _lib.DTYPE_BF16, 1.0, 1.0, ws, 16, None) == 3  # small ws
+    arr[1].left = None
+    assert lib.mfsdp_shampoo_stats(arr, 2, _lib.DTYPE_BF16, 1.0, 1.0, ws, 1 << 30, None) == 1
+    arr[1].left = 0x100000 + 8   # inside matrix 0's gradient
+    assert lib.mfsdp_shampoo_stats(arr, 2, _lib.DTYPE_BF16, 1.0, 1.0, ws, 1 << 30, None) == 4
+    arr[1].left = 0x500000
+    assert lib.mfsdp_shampoo_stats(arr, 2, _lib.DTYPE_BF16, float("nan"), 1.0, ws, 1 << 30,
+                                   None) == 1
+    arr[1].rows = 0
+    assert lib.mfsdp_stats_workspace_size(arr, 2, _lib.DTYPE_BF16, ctypes.byref(out)) == 1
+
+
+def test_fp32_iterate_byte_limit():
+    # 32768 x 32768 fp32 iterates would need 2^32-byte offsets: refused; bf16 fits
+    arr, _ = mats([(32768, 32768)])
+    st, _ = ws_size(arr, 1, _lib.DTYPE_F32)
+    assert st == 2
+    st, nb = ws_size(arr, 1, _lib.DTYPE_BF16)
+    assert st == 0 and nb > 0

@@ -55,11 +55,11 @@ def kernel_usage(remarks):
 
 
 def test_ns_kernels_use_no_scratch(device_build):
-    # every mode (gram, poly, update, wide and tall apply) in both dtypes
+    # every mode (gram, poly, update, wide and tall apply, statistics) in both dtypes
     _, remarks = device_build
     usage = kernel_usage(remarks)
     ns = {k: v for k, v in usage.items() if "ns_gemm_kernel" in k}
-    assert len(ns) == 10, list(usage)
+    assert len(ns) == 12, list(usage)
     for k, v in ns.items():
         assert v.get("ScratchSize", 0) == 0, (k, v)
         assert v.get("VGPRs Spill", 0) == 0, (k, v)
