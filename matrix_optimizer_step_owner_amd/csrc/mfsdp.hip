@@ -334,6 +334,7 @@ hipError_t enqueue_ns_group(const Plan& p, const Plan::Group& gr, const MatDesc*
     ep.cur = it & 1;
     ep.first = it == 0;
     ep.b_is_A = skip_poly ? 1 : 0;
+    ep.fold = skip_poly ? 0 : 1;
     ep.a = a;
     ep.b = b;
     ep.c = c;

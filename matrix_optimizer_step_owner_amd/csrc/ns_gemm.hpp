@@ -74,6 +74,8 @@ struct NsEpi {
   int cur;        // 0: the current iterate is X0, 1: X1
   int first;      // first iteration (apply the normalization factor)
   int b_is_A;     // c == 0: the update multiplies A (scaled by kb = b)
+  int fold;       // the poly stores B' = aI + bA + cA^2, so the update is
+                  // X' = B'X with no read of X in its epilogue
   float a, b, c;
   float kb;       // factor of the B X product in the update epilogue
   float decay;    // 1 - lr*wd
@@ -567,7 +569,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     for (int p = 0; p < 8; ++p) {
       int grow, gcol, sl, r_in, c_in;
       coordA(i, p, grow, gcol, sl, r_in, c_in);
-      if (MODE != kModeGram && MODE != kModeSyrk)
+      if (MODE != kModeGram && MODE != kModeSyrk && !(kUpd && ep.fold))
         xin[p] = load_raw8<E>(ein + static_cast<size_t>(grow) * ldo + gcol);
       if (wide_apply && vec && grow < d.m && gcol + 8 <= d.n)
         win[p] = load_raw8<E>(W + static_cast<size_t>(grow) * d.cols + gcol);
@@ -609,6 +611,14 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
         if (MODE == kModePoly) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = fmaf(ep.c, v[e], ep.b * x8[e]);
+          if (ep.fold && ti == tj) {   // + aI on the diagonal
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (grow == gcol + e) v[e] += ep.a;
+          }
+        } else if (ep.fold) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= alpha;
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = alpha * fmaf(ep.kb, v[e], ep.a * x8[e]);
