@@ -212,8 +212,10 @@ def main():
     hp = dict(lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov, weight_decay=wl.weight_decay,
               ns_steps=wl.ns_steps, abc=wl.abc)
 
+    muon = mf.MuonStep(W, G, M)
+
     def step():
-        mf.muon_step(W, G, M, workspace=ws, **hp)
+        muon.step(workspace=ws, **hp)
         mf.adamw_tail(P, Gt, Mt, Vt, lr=wl.adam_lr, beta1=wl.adam_beta1,
                       beta2=wl.adam_beta2, eps=wl.adam_eps,
                       weight_decay=wl.adam_weight_decay, step=wl.adam_step)

@@ -23,7 +23,7 @@ import torch
 from . import _lib
 from ._lib import MfsdpError, NS_EPS
 
-__all__ = ["muon_step", "adamw_tail", "muon_workspace_size", "default_scale",
+__all__ = ["muon_step", "MuonStep", "adamw_tail", "muon_workspace_size", "default_scale",
            "plan_owners", "tail_layout", "tail_pack", "tail_unpack", "shampoo_stats",
            "timing", "MfsdpError", "NS_EPS", "library_path"]
 
@@ -151,6 +151,70 @@ def muon_step(weights: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
                                    workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(),
                                    stream))
+
+
+class MuonStep:
+    """A validated, reusable owner-local Muon step over a fixed list of
+    matrices (mfsdp_muon_step without per-call marshalling).
+
+    The tensors are checked and their descriptors built once; each ``step``
+    call only passes the hyperparameters, torch's current stream and the
+    workspace to the C ABI.  The tensors must stay alive and in place (the same
+    storage) for the object's lifetime; their contents change freely.
+    """
+
+    def __init__(self, weights: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
+                 momenta: Sequence[torch.Tensor],
+                 scales: Optional[Sequence[float]] = None,
+                 update_out: Optional[Sequence[torch.Tensor]] = None):
+        n = len(weights)
+        if not (len(grads) == n and len(momenta) == n):
+            raise ValueError("weights, grads and momenta must have the same length")
+        if scales is not None and len(scales) != n:
+            raise ValueError("scales must have one entry per matrix")
+        if update_out is not None and len(update_out) != n:
+            raise ValueError("update_out must have one entry per matrix")
+        self._n = n
+        self._keep = (list(weights), list(grads), list(momenta),
+                      None if update_out is None else list(update_out))
+        if n == 0:
+            return
+        dtype = weights[0].dtype
+        if dtype not in _DTYPES:
+            raise TypeError(f"unsupported dtype {dtype}")
+        device = weights[0].device
+        if device.type != "cuda":
+            raise ValueError("MuonStep needs GPU tensors")
+        for i in range(n):
+            if weights[i].dim() != 2:
+                raise ValueError(f"weights[{i}] must be 2D")
+            _check_matrix(weights[i], f"weights[{i}]", dtype, device)
+            _check_matrix(grads[i], f"grads[{i}]", dtype, device, weights[i].shape)
+            _check_matrix(momenta[i], f"momenta[{i}]", dtype, device, weights[i].shape)
+            if update_out is not None and update_out[i] is not None:
+                _check_matrix(update_out[i], f"update_out[{i}]", torch.float32, device,
+                              weights[i].shape)
+        self._device = device
+        self._code = _DTYPES[dtype]
+        self._arr = _build_descs(weights, grads, momenta, scales, update_out)
+        need = ctypes.c_size_t(0)
+        _lib.check(_lib.load().mfsdp_muon_workspace_size(self._arr, n, self._code,
+                                                         ctypes.byref(need)))
+        self._need = need.value
+
+    def step(self, *, lr: float, beta: float = 0.95, nesterov: bool = True,
+             weight_decay: float = 0.0, ns_steps: int = 5, abc=(3.4445, -4.7750, 2.0315),
+             workspace: Optional[torch.Tensor] = None) -> None:
+        if self._n == 0:
+            return
+        stream = torch.cuda.current_stream(self._device).cuda_stream
+        if workspace is None:
+            workspace = _workspace(self._device, stream, self._need)
+        a, b, c = abc
+        _lib.check(_lib.load().mfsdp_muon_step(
+            self._arr, self._n, self._code, lr, beta, 1 if nesterov else 0, weight_decay,
+            ns_steps, a, b, c, workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), stream))
 
 
 def adamw_tail(p: torch.Tensor, g: torch.Tensor, m: torch.Tensor, v: torch.Tensor,

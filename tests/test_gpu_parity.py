@@ -194,3 +194,21 @@ def test_resume_equals_continuous():
     again.run(**hp)
     for i in range(len(Ws)):
         assert torch.equal(again.W[i], cont.W[i]) and torch.equal(again.M[i], cont.M[i])
+
+
+def test_prepared_step_object_equals_function():
+    # mf.MuonStep validates once and reuses its descriptors: two steps of it
+    # equal two calls of mf.muon_step, bitwise
+    Ws, Gs, Ms = _subset_inputs()
+    hp = muon_hparams()
+    a = GpuStep(Ws, Gs, Ms, update_mask=[False] * len(Ws))
+    for _ in range(2):
+        a.run(**hp)
+    b = GpuStep(Ws, Gs, Ms, update_mask=[False] * len(Ws))
+    obj = mf.MuonStep(b.W, b.G, b.M)
+    kw = {k: v for k, v in hp.items()}
+    for _ in range(2):
+        obj.step(**kw)
+    torch.cuda.synchronize()
+    for i in range(len(Ws)):
+        assert torch.equal(a.W[i], b.W[i]) and torch.equal(a.M[i], b.M[i]), i
