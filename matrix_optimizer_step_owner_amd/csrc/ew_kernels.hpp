@@ -38,22 +38,39 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
 
   if (d.vec_ok) {
     constexpr int VPR = T / V;                 // vectors per tile row
-    for (int e = tid; e < T * VPR; e += kThreads) {
+    constexpr int NV = T * VPR / kThreads;     // vectors per thread
+    // All of this thread's loads first (the stores to M may alias G and M as
+    // far as the compiler knows, so interleaving would serialize latency).
+    uint4 graw[NV], mraw[NV];
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int e = tid + it * kThreads;
+      const int r = e / VPR, cv = e % VPR;
+      const int sr = sr0 + r, sc = sc0 + cv * V;
+      if (sr < d.rows && sc < d.cols) {
+        const size_t off = static_cast<size_t>(sr) * d.cols + sc;
+        graw[it] = gld<uint4>(G + off);
+        mraw[it] = gld<uint4>(M + off);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int e = tid + it * kThreads;
       const int r = e / VPR, cv = e % VPR;
       const int sr = sr0 + r, sc = sc0 + cv * V;
       float u[V];
       if (sr < d.rows && sc < d.cols) {
         const size_t off = static_cast<size_t>(sr) * d.cols + sc;
         float g[V], mo[V], mn[V];
-        Vec16<E>::unpack(*reinterpret_cast<const uint4*>(G + off), g);
-        Vec16<E>::unpack(*reinterpret_cast<const uint4*>(M + off), mo);
+        Vec16<E>::unpack(graw[it], g);
+        Vec16<E>::unpack(mraw[it], mo);
 #pragma unroll
         for (int k = 0; k < V; ++k) {
           mn[k] = fmaf(beta, mo[k], g[k]);
           u[k] = nesterov ? fmaf(beta, mn[k], g[k]) : mn[k];
           ssq = fmaf(u[k], u[k], ssq);
         }
-        *reinterpret_cast<uint4*>(M + off) = Vec16<E>::pack(mn);
+        gst<uint4>(M + off, Vec16<E>::pack(mn));
       } else {
 #pragma unroll
         for (int k = 0; k < V; ++k) u[k] = 0.f;
@@ -88,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
 #pragma unroll
     for (int k = 0; k < V; ++k) u[k] = d.tall ? sU[jv * V + k][ii] : sU[ii][jv * V + k];
     const size_t off = static_cast<size_t>(i0 + ii) * d.n_pad + j0 + jv * V;
-    *reinterpret_cast<uint4*>(X0 + off) = Vec16<E>::pack(u);
+    gst<uint4>(X0 + off, Vec16<E>::pack(u));
   }
 
   // Deterministic block reduction of the sum of squares.
