@@ -14,9 +14,6 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 LIB_PATH = os.path.join(PKG_DIR, "libmfsdp.so")
 SOURCES = [os.path.join(PKG_DIR, "csrc", "mfsdp.hip")]
-HEADERS = [os.path.join(PKG_DIR, "csrc", f) for f in
-           ("common.hpp", "ew_kernels.hpp", "ns_gemm.hpp")] + \
-          [os.path.join(ROOT, "include", "mfsdp.h")]
 
 
 def hipcc() -> str:

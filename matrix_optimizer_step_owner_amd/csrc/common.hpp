@@ -11,6 +11,11 @@ namespace mfsdp {
 constexpr int kTile = 256;
 // Tile edge of the elementwise momentum kernel (divides kTile).
 constexpr int kEwTile = 64;
+// Momentum-kernel block in the caller's (stored) layout: 64 rows x 128
+// columns, so each row segment is 256 contiguous bytes (bf16).  In the wide
+// layout that is 64 x 128 for a wide matrix and 128 x 64 for a tall one.
+constexpr int kEwRows = 64;
+constexpr int kEwCols = 128;
 constexpr int kThreads = 256;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -78,6 +83,17 @@ __device__ __forceinline__ float4 gld<float4>(const void* p) {
 template <>
 __device__ __forceinline__ void gst<float4>(void* p, const float4& v) {
   *(MFSDP_GLOBAL f32x4_t*)(p) = f32x4_t{v.x, v.y, v.z, v.w};
+}
+
+// Streaming (non-temporal) 16-byte accesses, for data touched once per step:
+// they keep the caches for the data that is re-read.
+__device__ __forceinline__ uint4 gld_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const MFSDP_GLOBAL u32x4_t*)(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void gst_stream(void* p, const uint4& v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, (MFSDP_GLOBAL u32x4_t*)(p));
 }
 
 // Element traits: storage type, elements per 16-byte vector, conversions.
@@ -155,6 +171,7 @@ struct MatDesc {
   int32_t ew_tile0;   // first momentum-kernel tile of this matrix
   int32_t ew_tiles_j; // momentum-kernel tiles along the wide n axis
   int32_t ew_ntiles;  // momentum-kernel tiles of this matrix
+  int32_t ew_th, ew_tw;  // momentum-kernel tile height / width in the wide layout
   float lr_scale;     // lr * scale
   int32_t vec_ok;     // rows of W/G/M/upd start 16-byte aligned
 };

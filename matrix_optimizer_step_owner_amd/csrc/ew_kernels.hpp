@@ -11,15 +11,16 @@ namespace mfsdp {
 
 // Momentum M' = beta*M + G, Nesterov U = G + beta*M' (or U = M'), sum of U^2
 // per tile, and U stored into X0 in wide layout (transposed when rows > cols),
-// zero in the tile padding.  One 256-thread workgroup per 64x64 wide tile.
+// zero in the tile padding.  One 256-thread workgroup per block of 64 stored
+// rows x 128 stored columns (kEwRows x kEwCols).
 template <class E>
 __global__ __launch_bounds__(kThreads) void momentum_kernel(
     const MatDesc* __restrict__ descs, WorkList wl, double* __restrict__ partials,
     float beta, int nesterov) {
   using S = typename E::storage_t;
   constexpr int V = E::kVec;
-  constexpr int T = kEwTile;
-  __shared__ float sU[T][T + 1];
+  constexpr int SR = kEwRows, SC = kEwCols;
+  __shared__ float sU[SR][SC + 1];
   __shared__ float sRed[kThreads / 64];
 
   const int bid = blockIdx.x;
@@ -27,20 +28,23 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
   const MatDesc d = descs[wl.mat[item]];
   const int local = bid - wl.begin[item];
   const int ti = local / d.ew_tiles_j, tj = local % d.ew_tiles_j;
-  const int i0 = ti * T, j0 = tj * T;          // wide tile origin
-  const int sr0 = d.tall ? j0 : i0;            // stored-layout tile origin
+  const int i0 = ti * d.ew_th, j0 = tj * d.ew_tw;   // wide tile origin
+  const int sr0 = d.tall ? j0 : i0;                  // stored-layout block origin
   const int sc0 = d.tall ? i0 : j0;
   const int tid = threadIdx.x;
 
   const S* G = static_cast<const S*>(d.G);
   S* M = static_cast<S*>(d.M);
+  S* X0 = static_cast<S*>(d.X0);
   float ssq = 0.f;
 
   if (d.vec_ok) {
-    constexpr int VPR = T / V;                 // vectors per tile row
-    constexpr int NV = T * VPR / kThreads;     // vectors per thread
+    constexpr int VPR = SC / V;                 // vectors per stored row
+    constexpr int NV = SR * VPR / kThreads;     // vectors per thread
     // All of this thread's loads first (the stores to M may alias G and M as
     // far as the compiler knows, so interleaving would serialize latency).
+    // G, M' and U are streamed (non-temporal); M is loaded through the caches
+    // because its line is written back in place.
     uint4 graw[NV], mraw[NV];
 #pragma unroll
     for (int it = 0; it < NV; ++it) {
@@ -49,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
       const int sr = sr0 + r, sc = sc0 + cv * V;
       if (sr < d.rows && sc < d.cols) {
         const size_t off = static_cast<size_t>(sr) * d.cols + sc;
-        graw[it] = gld<uint4>(G + off);
+        graw[it] = gld_stream(G + off);
         mraw[it] = gld<uint4>(M + off);
       }
     }
@@ -70,17 +74,21 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
           u[k] = nesterov ? fmaf(beta, mn[k], g[k]) : mn[k];
           ssq = fmaf(u[k], u[k], ssq);
         }
-        gst<uint4>(M + off, Vec16<E>::pack(mn));
+        gst_stream(M + off, Vec16<E>::pack(mn));
       } else {
 #pragma unroll
         for (int k = 0; k < V; ++k) u[k] = 0.f;
       }
+      if (d.tall) {
 #pragma unroll
-      for (int k = 0; k < V; ++k) sU[r][cv * V + k] = u[k];
+        for (int k = 0; k < V; ++k) sU[r][cv * V + k] = u[k];
+      } else {  // same layout: straight to X0
+        gst_stream(X0 + static_cast<size_t>(i0 + r) * d.n_pad + j0 + cv * V, Vec16<E>::pack(u));
+      }
     }
   } else {
-    for (int e = tid; e < T * T; e += kThreads) {
-      const int r = e / T, cc = e % T;
+    for (int e = tid; e < SR * SC; e += kThreads) {
+      const int r = e / SC, cc = e % SC;
       const int sr = sr0 + r, sc = sc0 + cc;
       float u = 0.f;
       if (sr < d.rows && sc < d.cols) {
@@ -96,16 +104,27 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
   }
   __syncthreads();
 
-  // Store U into X0 (wide layout, rows 16-byte aligned, padding included).
-  S* X0 = static_cast<S*>(d.X0);
-  constexpr int VPR = T / V;
-  for (int e = tid; e < T * VPR; e += kThreads) {
-    const int ii = e / VPR, jv = e % VPR;
-    float u[V];
+  // Store U into X0 (wide layout, rows 16-byte aligned, padding included):
+  // wide row ii of the block is stored row ii (wide) or stored column ii (tall).
+  // The vector path of a wide matrix has already stored it.
+  if (!d.tall && !d.vec_ok) {
+    constexpr int VPR = SC / V;
+    for (int e = tid; e < SR * VPR; e += kThreads) {
+      const int ii = e / VPR, jv = e % VPR;
+      float u[V];
 #pragma unroll
-    for (int k = 0; k < V; ++k) u[k] = d.tall ? sU[jv * V + k][ii] : sU[ii][jv * V + k];
-    const size_t off = static_cast<size_t>(i0 + ii) * d.n_pad + j0 + jv * V;
-    gst<uint4>(X0 + off, Vec16<E>::pack(u));
+      for (int k = 0; k < V; ++k) u[k] = sU[ii][jv * V + k];
+      gst_stream(X0 + static_cast<size_t>(i0 + ii) * d.n_pad + j0 + jv * V, Vec16<E>::pack(u));
+    }
+  } else if (d.tall) {
+    constexpr int VPR = SR / V;
+    for (int e = tid; e < SC * VPR; e += kThreads) {
+      const int ii = e / VPR, jv = e % VPR;
+      float u[V];
+#pragma unroll
+      for (int k = 0; k < V; ++k) u[k] = sU[jv * V + k][ii];
+      gst_stream(X0 + static_cast<size_t>(i0 + ii) * d.n_pad + j0 + jv * V, Vec16<E>::pack(u));
+    }
   }
 
   // Deterministic block reduction of the sum of squares.
@@ -146,18 +165,17 @@ __global__ __launch_bounds__(kThreads) void apply_x0_kernel(
     const MatDesc* __restrict__ descs, WorkList wl, const float* __restrict__ scales,
     float decay) {
   using S = typename E::storage_t;
-  constexpr int T = kEwTile;
   const int bid = blockIdx.x;
   const int item = find_item(wl, bid);
   const int k = wl.mat[item];
   const MatDesc d = descs[k];
   const int local = bid - wl.begin[item];
-  const int i0 = (local / d.ew_tiles_j) * T, j0 = (local % d.ew_tiles_j) * T;
+  const int i0 = (local / d.ew_tiles_j) * d.ew_th, j0 = (local % d.ew_tiles_j) * d.ew_tw;
   const float s = scales[k];
   const S* X0 = static_cast<const S*>(d.X0);
   S* W = static_cast<S*>(d.W);
-  for (int e = threadIdx.x; e < T * T; e += kThreads) {
-    const int i = i0 + e / T, j = j0 + e % T;
+  for (int e = threadIdx.x; e < d.ew_th * d.ew_tw; e += kThreads) {
+    const int i = i0 + e / d.ew_tw, j = j0 + e % d.ew_tw;
     if (i >= d.m || j >= d.n) continue;
     const float o = s * E::to_f32(X0[static_cast<size_t>(i) * d.n_pad + j]);
     const size_t off = d.tall ? static_cast<size_t>(j) * d.cols + i

@@ -123,7 +123,7 @@ hipError_t launch(int kind, hipStream_t stream, F&& f) {
 struct MatGeom {
   int64_t rows, cols, m, n, m_pad, n_pad;
   bool tall;
-  int64_t ew_tiles_j, ew_ntiles;
+  int64_t ew_tiles_j, ew_ntiles, ew_th, ew_tw;
 };
 
 struct Plan {
@@ -183,8 +183,11 @@ mfsdp_status_t make_geom(const mfsdp_matrix_t& mt, int64_t idx, MatGeom* g, size
                 "matrix %lld: %lld x %lld exceeds the iterate size limit (2^31 elements, "
                 "2^32 bytes)",
                 (long long)idx, (long long)mt.rows, (long long)mt.cols);
-  g->ew_tiles_j = g->n_pad / kEwTile;
-  g->ew_ntiles = (g->m_pad / kEwTile) * g->ew_tiles_j;
+  // momentum blocks: kEwRows x kEwCols in the stored layout
+  g->ew_th = g->tall ? kEwCols : kEwRows;
+  g->ew_tw = g->tall ? kEwRows : kEwCols;
+  g->ew_tiles_j = g->n_pad / g->ew_tw;
+  g->ew_ntiles = (g->m_pad / g->ew_th) * g->ew_tiles_j;
   return MFSDP_OK;
 }
 
@@ -786,6 +789,8 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
     d.ew_tile0 = static_cast<int32_t>(ew_acc);
     d.ew_tiles_j = static_cast<int32_t>(g.ew_tiles_j);
     d.ew_ntiles = static_cast<int32_t>(g.ew_ntiles);
+    d.ew_th = static_cast<int32_t>(g.ew_th);
+    d.ew_tw = static_cast<int32_t>(g.ew_tw);
     d.lr_scale = lr * mt.scale;
     d.vec_ok = (g.cols % static_cast<int64_t>(16 / es)) == 0 ? 1 : 0;
     ew_acc += g.ew_ntiles;
