@@ -17,6 +17,13 @@ Usage (after copying the rocprofv3 output back):
   python -m matrix_optimizer_step_owner_amd.profiling traffic FETCH.csv WRITE.csv \
       --calib-mib 1024 --kernel update --workload block_d2048 \
       --command "<the profiled command>" --out profiles/update_kernel_block_d2048_traffic.json
+  python -m matrix_optimizer_step_owner_amd.profiling counters PMC1.csv PMC2.csv \
+      --calib-mib 1024 --command "<command 1>" --command "<command 2>" \
+      --out profiles/counters_<workload>.txt
+
+Any other ``--pmc`` counters in the files (GRBM_GUI_ACTIVE,
+SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16, TCC_HIT_sum, ...) are
+averaged per kernel kind by ``counters``.
 """
 
 from __future__ import annotations
@@ -111,6 +118,92 @@ def traffic(fetch_csv: str, write_csv: str, calib_bytes: int, kind: str) -> dict
     return res
 
 
+#: XCDs (GRBM_GUI_ACTIVE is reported once per XCD) and SIMDs of an MI355X
+N_XCD = 8
+N_SIMD = 256 * 4
+MIN_GRBM_US = 50.0
+
+
+def counter_table(pmc_csvs: List[str], calib: Dict[str, float]) -> List[dict]:
+    """Per kernel kind, the mean per dispatch of every counter in the files,
+    the kernel duration and what follows from them: SCLK (GRBM_GUI_ACTIVE per
+    XCD over the duration), MFMA busy % (busy SIMD-cycles over SIMD-cycles,
+    rocprofv3's MfmaUtil), executed bf16 MFMA flops (MOPS x 512) and
+    calibrated HBM bytes (FETCH_SIZE / WRITE_SIZE in KiB over ``calib``)."""
+    per: Dict[int, dict] = collections.OrderedDict()
+    for path in pmc_csvs:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (path, int(r["Dispatch_Id"]))
+                d = per.setdefault(key, {"kernel": r["Kernel_Name"], "c": {},
+                                         "dur_ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+                d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    kinds: Dict[str, List[dict]] = collections.OrderedDict()
+    for d in per.values():
+        k = short_name(d["kernel"]) or ("copy" if "copyBuffer" in d["kernel"] else "")
+        if k:
+            kinds.setdefault(k, []).append(d)
+    rows = []
+    for k, ds in kinds.items():
+        row = {"kind": k, "dispatches": len(ds), "avg_us": sum(d["dur_ns"] for d in ds) / len(ds) / 1e3}
+        names = sorted({n for d in ds for n in d["c"]})
+        for n in names:
+            vals = [d["c"][n] for d in ds if n in d["c"]]
+            row[n] = sum(vals) / len(vals)
+        dur_s = row["avg_us"] * 1e-6
+        # GRBM_GUI_ACTIVE spans the profiler's whole sampling window of a
+        # dispatch (some microseconds beyond the kernel), so the derived clock
+        # and busy fraction are only given for kernels of MIN_GRBM_US or more.
+        if "GRBM_GUI_ACTIVE" in row and row["avg_us"] >= MIN_GRBM_US:
+            cyc = row["GRBM_GUI_ACTIVE"] / N_XCD
+            row["sclk_ghz"] = cyc / dur_s / 1e9
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in row:
+                row["mfma_busy_pct"] = 100.0 * row["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD)
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in row and dur_s > 0:
+            row["mfma_tflops"] = row["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / dur_s / 1e12
+        for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+            if cn in row and cn in calib and dur_s > 0:
+                row[cn.lower() + "_mb"] = row[cn] * 1024.0 / calib[cn] / 1e6
+                row[cn.lower() + "_gbs"] = row[cn] * 1024.0 / calib[cn] / dur_s / 1e9
+        rows.append(row)
+    return rows
+
+
+def calibration(pmc_csvs: List[str], calib_bytes: int) -> Dict[str, float]:
+    """Counter units per byte of the largest plain copy dispatch in the files."""
+    out = {}
+    for path in pmc_csvs:
+        for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+            ds = counter_by_dispatch(path, cn)
+            copies = [d["value"] for d in ds if "copyBuffer" in d["kernel"]]
+            if copies:
+                out[cn] = max(copies) * 1024.0 / calib_bytes
+    return out
+
+
+def format_counters(rows: List[dict], commands: List[str], calib: Dict[str, float]) -> str:
+    out = ["rocprofv3 --pmc summary (means per dispatch)", "", "commands:"]
+    out += ["  " + c for c in commands]
+    out += ["", "calibration (counter KiB per byte of a plain copy): "
+            + (", ".join(f"{k} {v:.3f}" for k, v in calib.items()) or "none"),
+            "sclk = GRBM_GUI_ACTIVE per XCD / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /",
+            f"(GRBM_GUI_ACTIVE per XCD x {N_SIMD} SIMDs).  GRBM_GUI_ACTIVE spans the profiler's",
+            "dispatch window, some microseconds longer than the kernel, so both are given only",
+            f"for kernels of {MIN_GRBM_US:.0f} us or more and overstate sclk (understate busy) by",
+            "about that window over the duration.", "",
+            f"{'kind':12s} {'disp':>5s} {'avg us':>9s} {'sclk GHz':>9s} {'MFMA busy%':>10s} "
+            f"{'MFMA TF/s':>10s} {'fetch MB':>10s} {'write MB':>10s} {'HBM GB/s':>9s}"]
+    for r in rows:
+        def f(key, fmt):
+            return format(r[key], fmt) if key in r else "-"
+        hbm = (r.get("fetch_size_gbs", 0.0) + r.get("write_size_gbs", 0.0)) or None
+        out.append(f"{r['kind']:12s} {r['dispatches']:5d} {r['avg_us']:9.2f} {f('sclk_ghz', '9.2f'):>9s} "
+                   f"{f('mfma_busy_pct', '10.1f'):>10s} {f('mfma_tflops', '10.1f'):>10s} "
+                   f"{f('fetch_size_mb', '10.1f'):>10s} {f('write_size_mb', '10.1f'):>10s} "
+                   f"{format(hbm, '9.0f') if hbm else '-':>9s}")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(prog="python -m matrix_optimizer_step_owner_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -126,8 +219,19 @@ def main(argv=None) -> None:
     t.add_argument("--workload", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("pmc_csvs", nargs="+")
+    c.add_argument("--calib-mib", type=int, default=0)
+    c.add_argument("--command", action="append", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    if a.cmd == "stats":
+    if a.cmd == "counters":
+        cal = calibration(a.pmc_csvs, a.calib_mib << 20) if a.calib_mib else {}
+        text = format_counters(counter_table(a.pmc_csvs, cal), a.command, cal)
+        with open(a.out, "w") as f:
+            f.write(text)
+        print(text)
+    elif a.cmd == "stats":
         text = format_stats(kernel_stats(a.stats_csv), a.command)
         with open(a.out, "w") as f:
             f.write(text)

@@ -55,3 +55,39 @@ def test_stats_summary_and_cli(tmp_path):
     doc = json.loads(tj.read_text())
     assert doc["bytes_per_launch"] == 15.0 * 1024
     assert doc["source_sha256"] == profiling.kernel_source_hash()
+
+
+def test_counter_table_derived_columns(tmp_path):
+    """Clock, MFMA busy, executed flops and calibrated bytes from known counts."""
+    p = tmp_path / "c.csv"
+    dur_ns = 200_000  # 200 us
+    ghz = 2.0
+    cyc = ghz * 1e9 * dur_ns * 1e-9
+    with open(p, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                    "Start_Timestamp", "End_Timestamp"])
+        for i in range(2):
+            t0 = 1_000_000 * (i + 1)
+            # GRBM_GUI_ACTIVE summed over the 8 XCDs; MFMA busy on half of all SIMD-cycles
+            rows = [("GRBM_GUI_ACTIVE", cyc * profiling.N_XCD),
+                    ("SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * cyc * profiling.N_SIMD),
+                    ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 1e15 * dur_ns * 1e-9 / 512),  # 1 PFLOP/s
+                    ("FETCH_SIZE", 0.5 * 1000.0)]   # KiB, counter reads half the bytes
+            for name, v in rows:
+                w.writerow([i, UPD, name, v, t0, t0 + dur_ns])
+        w.writerow([9, COPY, "FETCH_SIZE", 0.5 * 1024, 0, 100])
+    cal = profiling.calibration([str(p)], 1 << 20)
+    assert abs(cal["FETCH_SIZE"] - 0.5) < 1e-12
+    rows = {r["kind"]: r for r in profiling.counter_table([str(p)], cal)}
+    u = rows["update"]
+    assert u["dispatches"] == 2 and abs(u["avg_us"] - 200.0) < 1e-9
+    assert abs(u["sclk_ghz"] - ghz) < 1e-9
+    assert abs(u["mfma_busy_pct"] - 50.0) < 1e-9
+    assert abs(u["mfma_tflops"] - 1000.0) < 1e-6
+    assert abs(u["fetch_size_mb"] - 1000.0 * 1024 / 1e6) < 1e-9
+    # short kernels get no GRBM-derived columns
+    assert "sclk_ghz" not in rows["copy"]
+    out = tmp_path / "c.txt"
+    profiling.main(["counters", str(p), "--calib-mib", "1", "--command", "x", "--out", str(out)])
+    assert "update" in out.read_text()
