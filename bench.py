@@ -11,6 +11,10 @@ the whole step (NS flops per step / wall time per step); ``ms_per_step`` is
 the step time.  The timed region runs the library exactly as a caller would
 (its Newton-Schulz stream groups included) with no per-kernel instrumentation.
 
+``cold_cache`` times single steps (hipEvents on the current stream) after
+overwriting 512 MiB, twice the MALL, so that no operand survives in cache from
+the step before; it gives the median and the minimum over up to 20 steps.
+
 ``roofline`` describes the dominant kernel (most GPU time per step).  It comes
 from a second pass of the same K steps right after the timed region, with the
 Newton-Schulz work on ONE stream (MFSDP_NS_GROUPS=1) so that no two kernels of
@@ -44,6 +48,10 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 KINDS = ("momentum", "norm", "gram", "poly", "update", "final", "apply", "adamw")
+#: cold-cache pass: bytes overwritten before each timed step (2x the 256 MB
+#: MALL) and the most steps it times
+FLUSH_BYTES = 512 << 20
+COLD_REPS = 20
 
 
 def ns_flops_by_kind(shapes):
@@ -233,6 +241,23 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    # cold-cache pass: each step timed alone with hipEvents on the current
+    # stream after overwriting a 512 MiB buffer (twice the 256 MB MALL), so
+    # no operand is cache-resident from the step before; median and minimum
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(min(args.steps, COLD_REPS)):
+        flush.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    cold.sort()
+
     # roofline pass: the same steps with the Newton-Schulz work on one stream
     saved = os.environ.get("MFSDP_NS_GROUPS")
     os.environ["MFSDP_NS_GROUPS"] = "1"
@@ -312,6 +337,8 @@ def main():
         if ns_kernel_ms else None,
         "pct_bf16_peak_step": round(100 * ns_flops_step / (ms_per_step * 1e-3) / 1e12 / peak, 2),
         "kernels": kernels,
+        "cold_cache": {"reps": len(cold), "flush_bytes": FLUSH_BYTES,
+                       "ms_median": round(cold[len(cold) // 2], 4), "ms_min": round(cold[0], 4)},
         "roofline": roof,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.workload,
                                                                       args.cpu_budget),
