@@ -136,7 +136,8 @@ struct Plan {
   // Newton-Schulz groups: matrices split into flop-balanced groups whose
   // iterations run on separate streams (see enqueue_muon).  Per group: its
   // matrices and the offsets/counts of its tile tables (in int2 entries from
-  // off_tiles): symmetric, update, final-wide, final-tall.
+  // off_tiles): symmetric (Gram and polynomial), update, final-wide,
+  // final-tall.
   struct Group {
     std::vector<int64_t> mats;
     int64_t sym = 0, upd = 0, fin_wide = 0, fin_tall = 0;
@@ -144,6 +145,29 @@ struct Plan {
   };
   std::vector<Group> groups;
 };
+
+// Tile table of one launch over matrices `mats`: by decreasing k_of (stable),
+// tiles_of(i) tiles per matrix, balanced over the XCDs when `balance` (else in
+// that sorted order).
+template <class KOf, class TilesOf>
+void launch_order(std::vector<int64_t> mats, KOf k_of, TilesOf tiles_of, bool balance,
+                  int2* out) {
+  std::stable_sort(mats.begin(), mats.end(),
+                   [&](int64_t x, int64_t y) { return k_of(x) > k_of(y); });
+  std::vector<int2> seq;
+  std::vector<int64_t> cost;
+  for (int64_t i : mats) {
+    const int64_t nt = tiles_of(i);
+    for (int64_t q = 0; q < nt; ++q) {
+      seq.push_back(make_int2(static_cast<int>(i), static_cast<int>(q)));
+      cost.push_back(k_of(i));
+    }
+  }
+  if (balance)
+    xcd_balance(seq, cost, kXcds, out);
+  else
+    std::copy(seq.begin(), seq.end(), out);
+}
 
 // Work-group count that one launch needs to fill the MI355X (256 CUs).
 constexpr int64_t kCus = 256;
@@ -618,13 +642,21 @@ mfsdp_status_t stats_impl(const mfsdp_stats_matrix_t* mats, int64_t n, mfsdp_dty
       s.m = static_cast<int32_t>(side == 0 ? m.rows : m.cols);
       s.m_pad = static_cast<int32_t>(side == 0 ? p.r_pad[i] : p.c_pad[i]);
       s.n_pad = static_cast<int32_t>(side == 0 ? p.c_pad[i] : p.r_pad[i]);
-      const int64_t tm = s.m_pad / kTile;
-      for (int64_t q = 0; q < tm * (tm + 1) / 2; ++q)
-        *tab++ = make_int2(static_cast<int>(k), static_cast<int>(q));
       ++k;
     }
   }
   lists[2 * n] = static_cast<int32_t>(acc);
+  {
+    std::vector<int64_t> all(static_cast<size_t>(k));
+    for (int64_t j = 0; j < k; ++j) all[j] = j;
+    launch_order(
+        all, [&](int64_t j) { return static_cast<int64_t>(syrk[j].n_pad); },
+        [&](int64_t j) {
+          const int64_t tm = syrk[j].m_pad / kTile;
+          return tm * (tm + 1) / 2;
+        },
+        true, tab);
+  }
   hipError_t e = hipMemcpyAsync(ws, blob.data(), p.blob_bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "descriptor upload: %s", hipGetErrorString(e));
   e = dtype == MFSDP_DTYPE_BF16 ? enqueue_stats<ElemBF16>(p, n, ws, alpha, beta, stream)
@@ -808,38 +840,33 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
     }
     begin[n_mats] = static_cast<int32_t>(acc);
   }
-  // per-group tile tables; within a launch, matrices with the longest K
-  // first (they are dispatched first and set the launch's critical path)
+  // per-group tile tables: each launch's tiles by decreasing K (a matrix's
+  // tiles together), balanced over the XCDs when one stream runs every
+  // launch.  With several stream groups (launches of about one round of
+  // tiles, run concurrently) the plain sorted order measured faster: there
+  // the launches of the other groups fill the CUs left idle.
   {
+    const bool balance = p.groups.size() == 1;
     int2* tab = reinterpret_cast<int2*>(blob.data() + p.off_tiles);
+    auto sym_tiles = [&](int64_t i) {
+      const int64_t tm = p.geom[i].m_pad / kTile;
+      return tm * (tm + 1) / 2;
+    };
+    auto all_tiles = [&](int64_t i) {
+      return (p.geom[i].m_pad / kTile) * (p.geom[i].n_pad / kTile);
+    };
+    // The Gram (K = n) and polynomial (K = m) launches share one table: by
+    // decreasing n, then m, in runs of equal (n, m), so that both K are
+    // balanced over the XCDs.
+    auto k_sym = [&](int64_t i) { return (p.geom[i].n_pad << 24) | p.geom[i].m_pad; };
+    auto k_mm = [&](int64_t i) { return p.geom[i].m_pad; };   // update, apply
     for (const Plan::Group& gr : p.groups) {
-      std::vector<int64_t> by_n(gr.mats), by_m(gr.mats);
-      std::stable_sort(by_n.begin(), by_n.end(), [&](int64_t x, int64_t y) {
-        return p.geom[x].n_pad > p.geom[y].n_pad;
-      });
-      std::stable_sort(by_m.begin(), by_m.end(), [&](int64_t x, int64_t y) {
-        return p.geom[x].m_pad > p.geom[y].m_pad;
-      });
-      int2* t = tab + gr.t_sym;
-      for (int64_t i : by_n) {
-        const int64_t tm = p.geom[i].m_pad / kTile;
-        for (int64_t q = 0; q < tm * (tm + 1) / 2; ++q)
-          *t++ = make_int2(static_cast<int>(i), static_cast<int>(q));
-      }
-      t = tab + gr.t_upd;
-      for (int64_t i : by_m) {
-        const int64_t nt = (p.geom[i].m_pad / kTile) * (p.geom[i].n_pad / kTile);
-        for (int64_t q = 0; q < nt; ++q) *t++ = make_int2(static_cast<int>(i), static_cast<int>(q));
-      }
-      for (int tall = 0; tall <= 1; ++tall) {
-        t = tab + (tall ? gr.t_fin_tall : gr.t_fin_wide);
-        for (int64_t i : by_m) {
-          if (p.geom[i].tall != (tall == 1)) continue;
-          const int64_t nt = (p.geom[i].m_pad / kTile) * (p.geom[i].n_pad / kTile);
-          for (int64_t q = 0; q < nt; ++q)
-            *t++ = make_int2(static_cast<int>(i), static_cast<int>(q));
-        }
-      }
+      std::vector<int64_t> wide, tall;
+      for (int64_t i : gr.mats) (p.geom[i].tall ? tall : wide).push_back(i);
+      launch_order(gr.mats, k_sym, sym_tiles, balance, tab + gr.t_sym);
+      launch_order(gr.mats, k_mm, all_tiles, balance, tab + gr.t_upd);
+      launch_order(wide, k_mm, all_tiles, balance, tab + gr.t_fin_wide);
+      launch_order(tall, k_mm, all_tiles, balance, tab + gr.t_fin_tall);
     }
   }
 

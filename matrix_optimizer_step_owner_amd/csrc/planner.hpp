@@ -1,4 +1,4 @@
-// Host-side owner planner and packed-tail layout.
+// Host-side owner planner, packed-tail layout and launch tile order.
 //
 // Source: "MatrixFSDP: communication-free matrix optimizers under ZeRO-3
 // parameter sharding" -- arxivlens page, Summary (a balance-aware owner
@@ -76,6 +76,39 @@ inline int64_t tail_layout(const int64_t* numel, int64_t n, int64_t* offsets) {
     off += (numel[i] + kTailAlign - 1) / kTailAlign * kTailAlign;
   }
   return off;
+}
+
+// Order of the tiles of one grouped launch.  The device remaps workgroups so
+// that XCD x runs the contiguous logical range [x*q + min(x, r), +q + (x < r))
+// of the T tiles (q = T / n_xcd, r = T % n_xcd), in order.  The tiles come
+// sorted by decreasing cost (K length; the longest are dispatched first).
+// Each run of equal cost is cut into n_xcd contiguous parts, one per XCD,
+// whose sizes differ by at most one, the larger parts rotating over the XCDs
+// from run to run.  Every XCD thus gets the same mix of long and short tiles,
+// longest first, in runs of neighbouring tiles (shared operand panels stay in
+// its L2).  A plain sorted list would put all the long tiles on the first XCDs
+// and leave the others idle once their short tiles are done.
+template <class Entry>
+void xcd_balance(const std::vector<Entry>& tiles, const std::vector<int64_t>& cost, int n_xcd,
+                 Entry* out) {
+  const int64_t T = static_cast<int64_t>(tiles.size());
+  std::vector<std::vector<Entry>> per(n_xcd);
+  int rot = 0;
+  for (int64_t b = 0; b < T;) {
+    int64_t e = b;
+    while (e < T && cost[e] == cost[b]) ++e;
+    const int64_t nc = e - b, each = nc / n_xcd;
+    const int extra = static_cast<int>(nc % n_xcd);
+    int64_t idx = b;
+    for (int x = 0; x < n_xcd; ++x) {
+      const int64_t take = each + (((x - rot + n_xcd) % n_xcd) < extra ? 1 : 0);
+      per[x].insert(per[x].end(), tiles.begin() + idx, tiles.begin() + idx + take);
+      idx += take;
+    }
+    rot = (rot + extra) % n_xcd;
+    b = e;
+  }
+  for (const std::vector<Entry>& v : per) out = std::copy(v.begin(), v.end(), out);
 }
 
 }  // namespace mfsdp
