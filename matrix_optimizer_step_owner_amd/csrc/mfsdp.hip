@@ -147,11 +147,9 @@ struct Plan {
 };
 
 // Tile table of one launch over matrices `mats`: by decreasing k_of (stable),
-// tiles_of(i) tiles per matrix, balanced over the XCDs when `balance` (else in
-// that sorted order).
+// tiles_of(i) tiles per matrix, balanced over the XCDs.
 template <class KOf, class TilesOf>
-void launch_order(std::vector<int64_t> mats, KOf k_of, TilesOf tiles_of, bool balance,
-                  int2* out) {
+void launch_order(std::vector<int64_t> mats, KOf k_of, TilesOf tiles_of, int2* out) {
   std::stable_sort(mats.begin(), mats.end(),
                    [&](int64_t x, int64_t y) { return k_of(x) > k_of(y); });
   std::vector<int2> seq;
@@ -163,10 +161,7 @@ void launch_order(std::vector<int64_t> mats, KOf k_of, TilesOf tiles_of, bool ba
       cost.push_back(k_of(i));
     }
   }
-  if (balance)
-    xcd_balance(seq, cost, kXcds, out);
-  else
-    std::copy(seq.begin(), seq.end(), out);
+  xcd_balance(seq, cost, kXcds, out);
 }
 
 // Work-group count that one launch needs to fill the MI355X (256 CUs).
@@ -181,7 +176,7 @@ int choose_groups(int64_t n, int64_t upd_total) {
   const int64_t rounds = upd_total / kCus;
   if (upd_total < kCus / 4) g = 1;          // latency-bound; not worth streams
   else if (rounds >= 6) g = 1;
-  else g = 3;
+  else g = 2;
   if (const char* env = getenv("MFSDP_NS_GROUPS")) {
     const int v = atoi(env);
     if (v >= 1 && v <= kMaxGroups) g = v;
@@ -655,7 +650,7 @@ mfsdp_status_t stats_impl(const mfsdp_stats_matrix_t* mats, int64_t n, mfsdp_dty
           const int64_t tm = syrk[j].m_pad / kTile;
           return tm * (tm + 1) / 2;
         },
-        true, tab);
+        tab);
   }
   hipError_t e = hipMemcpyAsync(ws, blob.data(), p.blob_bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "descriptor upload: %s", hipGetErrorString(e));
@@ -841,12 +836,8 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
     begin[n_mats] = static_cast<int32_t>(acc);
   }
   // per-group tile tables: each launch's tiles by decreasing K (a matrix's
-  // tiles together), balanced over the XCDs when one stream runs every
-  // launch.  With several stream groups (launches of about one round of
-  // tiles, run concurrently) the plain sorted order measured faster: there
-  // the launches of the other groups fill the CUs left idle.
+  // tiles together), balanced over the XCDs
   {
-    const bool balance = p.groups.size() == 1;
     int2* tab = reinterpret_cast<int2*>(blob.data() + p.off_tiles);
     auto sym_tiles = [&](int64_t i) {
       const int64_t tm = p.geom[i].m_pad / kTile;
@@ -863,10 +854,10 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
     for (const Plan::Group& gr : p.groups) {
       std::vector<int64_t> wide, tall;
       for (int64_t i : gr.mats) (p.geom[i].tall ? tall : wide).push_back(i);
-      launch_order(gr.mats, k_sym, sym_tiles, balance, tab + gr.t_sym);
-      launch_order(gr.mats, k_mm, all_tiles, balance, tab + gr.t_upd);
-      launch_order(wide, k_mm, all_tiles, balance, tab + gr.t_fin_wide);
-      launch_order(tall, k_mm, all_tiles, balance, tab + gr.t_fin_tall);
+      launch_order(gr.mats, k_sym, sym_tiles, tab + gr.t_sym);
+      launch_order(gr.mats, k_mm, all_tiles, tab + gr.t_upd);
+      launch_order(wide, k_mm, all_tiles, tab + gr.t_fin_wide);
+      launch_order(tall, k_mm, all_tiles, tab + gr.t_fin_tall);
     }
   }
 
