@@ -247,9 +247,13 @@ __device__ __forceinline__ int kswz(int row) { return (row >> 2) & 3; }
 
 // Which DMA piece (0..7, or -1 for none) a K step issues in MFMA slot idx of
 // sub-step sub: the eight 1 KB pieces of a stage are spread over the step so
-// that the vector-memory queue never holds up the MFMA issue for long.
+// that the vector-memory queue never holds up the MFMA issue for long.  The
+// default (2) issues one piece every fourth slot of both sub-steps: the four
+// waves of a CU share one texture addresser, which the bunched schedules (0:
+// the first eight slots of sub-step 0; 1: every other slot of sub-step 0)
+// keep busy long enough to stall MFMA issue (3% slower on the d=2048 block).
 #ifndef MFSDP_DMA_SCHED
-#define MFSDP_DMA_SCHED 0
+#define MFSDP_DMA_SCHED 2
 #endif
 __host__ __device__ constexpr int dma_slot_piece(int sub, int idx) {
 #if MFSDP_DMA_SCHED == 0
