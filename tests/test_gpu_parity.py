@@ -178,6 +178,23 @@ def test_bitwise_determinism_and_grouping():
         assert torch.equal(r.W[j], a.W[i]) and torch.equal(r.U[j], a.U[i]), i
 
 
+def test_stream_group_count_is_bitwise_invariant(monkeypatch):
+    # 1 to 4 Newton-Schulz stream groups (the library picks 2 for this list)
+    Ws, Gs, Ms = _subset_inputs()
+    hp = muon_hparams()
+    ref = None
+    for groups in ("1", "2", "3", "4"):
+        monkeypatch.setenv("MFSDP_NS_GROUPS", groups)
+        st = GpuStep(Ws, Gs, Ms)
+        st.run(**hp)
+        if ref is None:
+            ref = st
+            continue
+        for i in range(len(Ws)):
+            assert torch.equal(st.W[i], ref.W[i]) and torch.equal(st.U[i], ref.U[i]), (groups, i)
+            assert torch.equal(st.M[i], ref.M[i]), (groups, i)
+
+
 def test_resume_equals_continuous():
     Ws, Gs, Ms = _subset_inputs()
     hp = muon_hparams()
