@@ -165,6 +165,76 @@ def stats_bench(args, wl, dev):
     }), flush=True)
 
 
+def adamw_cpu_baseline(n_sample, hp):
+    """The float64 AdamW oracle on an n_sample-element tail on the host cores."""
+    import oracle
+    rng = np.random.default_rng(1)
+    p, g, m = (rng.standard_normal(n_sample) * s for s in (0.02, 1e-3, 1e-3))
+    v = (rng.standard_normal(n_sample) * 1e-3) ** 2
+    reps, t_total = 0, 0.0
+    while t_total < 5.0 and reps < 50:
+        t0 = time.perf_counter()
+        oracle.adamw_tail(p, g, m, v, **hp)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(reps * n_sample * 28 / t_total / 1e9, 2), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"float64 numpy AdamW oracle on a {n_sample}-element tail, {reps} reps, "
+                      f"{t_total:.1f} s, 28 algorithmic bytes per element"}
+
+
+def adamw_bench(args, dev):
+    """Time mfsdp_adamw_tail alone on an n-element packed fp32 tail (one JSON line).
+
+    Algorithmic bytes: 28 per element (read p, g, m, v; write p, m, v).  The
+    tail state is a warm one: p ~ N(0, 0.02), g, m ~ N(0, 1e-3), v = N(0, 1e-3)^2,
+    drawn on the device from a seeded generator, step 10.
+    """
+    import matrix_optimizer_step_owner_amd as mf
+    n = args.adamw_elements
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    P, Gt, Mt, Vt = (torch.randn(n, generator=gen, device=dev) * s
+                     for s in (0.02, 1e-3, 1e-3, 1e-3))
+    Vt.mul_(Vt)
+    hp = dict(lr=0.02, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.01, step=10)
+
+    def step():
+        mf.adamw_tail(P, Gt, Mt, Vt, **hp)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    mf.timing.reset()
+    mf.timing.enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    mf.timing.enable(False)
+    tot, cnt = mf.timing.read("adamw")
+    avg_ms = tot / cnt
+    nbytes = 28 * n
+    ach = nbytes / (avg_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "AdamW tail GB/s (28 algorithmic bytes per element)",
+        "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"adamw_tail_{n}", "elements": n, "step": hp["step"]},
+        "kernels": {"adamw": {"avg_ms": round(avg_ms, 5), "gbs": round(ach, 1)}},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ach / PEAK_HBM_GBS, "kernel": "adamw", "traffic": None},
+        "cpu_baseline": None if args.no_cpu_baseline else adamw_cpu_baseline(
+            min(n, 1 << 24), hp),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +252,9 @@ def main():
     ap.add_argument("--shampoo-stats", action="store_true",
                     help="measure the Shampoo-type statistics update (L += G G^T, "
                          "R += G^T G) on the workload's gradients instead of the Muon step")
+    ap.add_argument("--adamw-elements", type=int, default=0,
+                    help="measure mfsdp_adamw_tail alone on a packed fp32 tail of this many "
+                         "elements instead of the Muon step")
     ap.add_argument("--ns-groups", type=int, default=0,
                     help="Newton-Schulz stream groups in the timed region (0: the library's "
                          "own choice)")
@@ -204,6 +277,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.adamw_elements > 0:
+        adamw_bench(args, dev)
+        return
     wl = wlm.WORKLOADS[args.workload]
     if args.shampoo_stats:
         stats_bench(args, wl, dev)

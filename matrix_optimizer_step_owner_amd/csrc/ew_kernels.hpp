@@ -204,24 +204,46 @@ __device__ __forceinline__ void adamw_elem(float& p, float g, float& m, float& v
   p = fmaf(-a.step_size, m / denom, p * a.decay);
 }
 
+// Each thread owns U 16-byte groups of every array, kThreads groups apart
+// (coalesced per unrolled step); all its loads are issued before any
+// arithmetic or store.  g and the new p, m, v are always streamed
+// (non-temporal).  Large tails (U = 4) stream the loads of p, m and v too:
+// 6.0 against 5.6 TB/s at 2^28 elements.  Small tails (U = 1, more
+// workgroups per CU) read p, m and v through the caches, which keeps a tail
+// that is still resident in the MALL from the previous step there.
+template <int U, bool kStreamState>
 __global__ __launch_bounds__(kThreads) void adamw_kernel(
     float* __restrict__ p, const float* __restrict__ g, float* __restrict__ m,
     float* __restrict__ v, int64_t n, AdamWArgs a) {
   const int64_t n4 = n >> 2;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t q = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; q < n4;
-       q += stride) {
-    float4 pp = reinterpret_cast<float4*>(p)[q];
-    const float4 gg = reinterpret_cast<const float4*>(g)[q];
-    float4 mm = reinterpret_cast<float4*>(m)[q];
-    float4 vv = reinterpret_cast<float4*>(v)[q];
-    adamw_elem(pp.x, gg.x, mm.x, vv.x, a);
-    adamw_elem(pp.y, gg.y, mm.y, vv.y, a);
-    adamw_elem(pp.z, gg.z, mm.z, vv.z, a);
-    adamw_elem(pp.w, gg.w, mm.w, vv.w, a);
-    reinterpret_cast<float4*>(p)[q] = pp;
-    reinterpret_cast<float4*>(m)[q] = mm;
-    reinterpret_cast<float4*>(v)[q] = vv;
+  const int64_t q0 = static_cast<int64_t>(blockIdx.x) * (kThreads * U) + threadIdx.x;
+  auto ld = [](const float* x) { return kStreamState ? gld_stream(x) : gld<uint4>(x); };
+  uint4 pr[U], gr[U], mr[U], vr[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t q = q0 + u * kThreads;
+    if (q < n4) {
+      pr[u] = ld(p + 4 * q);
+      gr[u] = gld_stream(g + 4 * q);
+      mr[u] = ld(m + 4 * q);
+      vr[u] = ld(v + 4 * q);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t q = q0 + u * kThreads;
+    if (q < n4) {
+      float pp[4], gg[4], mm[4], vv[4];
+      Vec16<ElemF32>::unpack(pr[u], pp);
+      Vec16<ElemF32>::unpack(gr[u], gg);
+      Vec16<ElemF32>::unpack(mr[u], mm);
+      Vec16<ElemF32>::unpack(vr[u], vv);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) adamw_elem(pp[k], gg[k], mm[k], vv[k], a);
+      gst_stream(p + 4 * q, Vec16<ElemF32>::pack(pp));
+      gst_stream(m + 4 * q, Vec16<ElemF32>::pack(mm));
+      gst_stream(v + 4 * q, Vec16<ElemF32>::pack(vv));
+    }
   }
   if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
     const int64_t i = (n4 << 2) + threadIdx.x;
@@ -232,5 +254,9 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(
     v[i] = vv;
   }
 }
+
+// Tails of at least this many 16-byte groups take the unrolled, fully
+// streamed kernel (8M elements: 8 workgroups per CU of 4 groups per thread).
+constexpr int64_t kAdamLargeGroups = int64_t(1) << 21;
 
 }  // namespace mfsdp

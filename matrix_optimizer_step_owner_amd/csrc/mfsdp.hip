@@ -915,11 +915,18 @@ static mfsdp_status_t adamw_tail_impl(float* param, const float* grad, float* ex
   args.step_size = static_cast<float>(static_cast<double>(lr) / bc1);
   args.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
   args.eps = eps;
-  const int64_t groups = std::max<int64_t>((n >> 2), 1);
-  const int64_t blocks = std::min<int64_t>((groups + kThreads - 1) / kThreads, 16384);
+  // one workgroup per kThreads * U 16-byte groups; at least one for the
+  // n % 4 remainder
+  const bool large = (n >> 2) >= kAdamLargeGroups;
+  const int64_t per_block = int64_t(kThreads) * (large ? 4 : 1);
+  const int64_t blocks = std::max<int64_t>(((n >> 2) + per_block - 1) / per_block, 1);
   hipError_t e = launch(MFSDP_KERNEL_ADAMW, stream, [&] {
-    adamw_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream>>>(
-        param, grad, exp_avg, exp_avg_sq, n, args);
+    if (large)
+      adamw_kernel<4, true><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream>>>(
+          param, grad, exp_avg, exp_avg_sq, n, args);
+    else
+      adamw_kernel<1, false><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream>>>(
+          param, grad, exp_avg, exp_avg_sq, n, args);
   });
   if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "adamw launch: %s", hipGetErrorString(e));
   return MFSDP_OK;

@@ -55,10 +55,40 @@ def test_adamw_workload_tails(key):
                 beta2=wl.adam_beta2, eps=wl.adam_eps, wd=wl.adam_weight_decay, label=key)
 
 
-@pytest.mark.parametrize("n", [1, 3, 5, 255, 1023, 4097, 1 << 20])
+@pytest.mark.parametrize("n", [1, 3, 5, 255, 1023, 4097, 1 << 20, (1 << 23) - 1, (1 << 23) + 3])
 def test_adamw_ragged_and_warm_state(n):
     p, g, m, v = wlm.random_tail_state(n, seed=n)
     adamw_check(p, g, m, v, step=10, label="warm")
+
+
+def test_adamw_large_tail_sampled():
+    # 2^28 + 3 elements (4 GiB of state, the bench's informational size, with
+    # a ragged end): the unrolled, fully streamed kernel, four 16-byte groups
+    # per thread, indices past 2^28; sampled elements, both ends included,
+    # against the oracle, and the step is deterministic.
+    n = (1 << 28) + 3
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    P, Gd, Md, Vd = (torch.randn(n, generator=gen, device=dev) * s
+                     for s in (0.02, 1e-3, 1e-3, 1e-3))
+    Vd.mul_(Vd)
+    rng = np.random.default_rng(5)
+    idx = np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n),
+                                    rng.integers(0, n, 200_000)]))
+    it = torch.from_numpy(idx).to(dev)
+    before = [f64(t[it]) for t in (P, Gd, Md, Vd)]
+    hp = dict(lr=0.02, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.01, step=10)
+    P2, M2, V2 = P.clone(), Md.clone(), Vd.clone()
+    mf.adamw_tail(P, Gd, Md, Vd, **hp)
+    mf.adamw_tail(P2, Gd, M2, V2, **hp)
+    torch.cuda.synchronize()
+    assert torch.equal(P, P2) and torch.equal(Md, M2) and torch.equal(Vd, V2)
+    del P2, M2, V2
+    pr, mr, vr = oracle.adamw_tail(*before, **hp)
+    ep, em, ev = rel(f64(P[it]), pr), rel(f64(Md[it]), mr), rel(f64(Vd[it]), vr)
+    say(f"adamw large n={n} sampled {idx.size}: rel p={ep:.2e} m={em:.2e} v={ev:.2e}")
+    assert ep <= ADAMW_TOL and em <= ADAMW_TOL and ev <= ADAMW_TOL
 
 
 def test_adamw_empty_tail():
