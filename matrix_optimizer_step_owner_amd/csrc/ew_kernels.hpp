@@ -20,8 +20,25 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
   using S = typename E::storage_t;
   constexpr int V = E::kVec;
   constexpr int SR = kEwRows, SC = kEwCols;
-  __shared__ float sU[SR][SC + 1];
+  // U staged in the storage type (values rounded as X0 stores them): 16.6 KB
+  // in bf16, so eight workgroups fit a CU.  Rows padded to 65 (bf16) or 129
+  // (fp32) 4-byte words: both the row-wise writes and the column-wise reads
+  // are free of bank conflicts.
+  constexpr int kPad = 4 / static_cast<int>(sizeof(S));
+  __shared__ S sU[SR][SC + kPad];
   __shared__ float sRed[kThreads / 64];
+  // 16 bytes of staged storage elements -> one vector
+  auto pack_raw = [](const S (&w)[V]) -> uint4 {
+    if constexpr (V == 8) {
+      return make_uint4(w[0] | (static_cast<uint32_t>(w[1]) << 16),
+                        w[2] | (static_cast<uint32_t>(w[3]) << 16),
+                        w[4] | (static_cast<uint32_t>(w[5]) << 16),
+                        w[6] | (static_cast<uint32_t>(w[7]) << 16));
+    } else {
+      return make_uint4(__float_as_uint(w[0]), __float_as_uint(w[1]), __float_as_uint(w[2]),
+                        __float_as_uint(w[3]));
+    }
+  };
 
   const int bid = blockIdx.x;
   const int item = find_item(wl, bid);
@@ -79,9 +96,13 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
 #pragma unroll
         for (int k = 0; k < V; ++k) u[k] = 0.f;
       }
-      if (d.tall) {
-#pragma unroll
-        for (int k = 0; k < V; ++k) sU[r][cv * V + k] = u[k];
+      if (d.tall) {   // four 4-byte words at word cv*4 of staged row r
+        const uint4 pk = Vec16<E>::pack(u);
+        uint32_t* row = reinterpret_cast<uint32_t*>(&sU[r][0]) + cv * 4;
+        row[0] = pk.x;
+        row[1] = pk.y;
+        row[2] = pk.z;
+        row[3] = pk.w;
       } else {  // same layout: straight to X0
         gst_stream(X0 + static_cast<size_t>(i0 + r) * d.n_pad + j0 + cv * V, Vec16<E>::pack(u));
       }
@@ -99,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
         ssq = fmaf(u, u, ssq);
         M[off] = E::from_f32(mn);
       }
-      sU[r][cc] = u;
+      sU[r][cc] = E::from_f32(u);
     }
   }
   __syncthreads();
@@ -111,19 +132,19 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
     constexpr int VPR = SC / V;
     for (int e = tid; e < SR * VPR; e += kThreads) {
       const int ii = e / VPR, jv = e % VPR;
-      float u[V];
+      S w[V];
 #pragma unroll
-      for (int k = 0; k < V; ++k) u[k] = sU[ii][jv * V + k];
-      gst_stream(X0 + static_cast<size_t>(i0 + ii) * d.n_pad + j0 + jv * V, Vec16<E>::pack(u));
+      for (int k = 0; k < V; ++k) w[k] = sU[ii][jv * V + k];
+      gst_stream(X0 + static_cast<size_t>(i0 + ii) * d.n_pad + j0 + jv * V, pack_raw(w));
     }
   } else if (d.tall) {
     constexpr int VPR = SR / V;
     for (int e = tid; e < SC * VPR; e += kThreads) {
       const int ii = e / VPR, jv = e % VPR;
-      float u[V];
+      S w[V];
 #pragma unroll
-      for (int k = 0; k < V; ++k) u[k] = sU[jv * V + k][ii];
-      gst_stream(X0 + static_cast<size_t>(i0 + ii) * d.n_pad + j0 + jv * V, Vec16<E>::pack(u));
+      for (int k = 0; k < V; ++k) w[k] = sU[jv * V + k][ii];
+      gst_stream(X0 + static_cast<size_t>(i0 + ii) * d.n_pad + j0 + jv * V, pack_raw(w));
     }
   }
 
