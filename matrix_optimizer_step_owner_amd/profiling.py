@@ -39,7 +39,8 @@ from typing import Dict, List
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 
-_NS_MODES = {"0": "gram", "1": "poly", "2": "update", "3": "final_wide", "4": "final_tall"}
+_NS_MODES = {"0": "gram", "1": "poly", "2": "update", "3": "final_wide", "4": "final_tall",
+             "5": "syrk"}
 
 
 def kernel_source_hash() -> str:

@@ -22,6 +22,9 @@ def test_short_names():
     assert profiling.short_name(UPD) == "update"
     assert profiling.short_name(UPD.replace("ElemBF16, 2", "ElemF32, 0")) == "gram_f32"
     assert profiling.short_name("mfsdp::adamw_kernel(float*)") == "adamw"
+    assert profiling.short_name("void mfsdp::adamw_kernel<4, true>(float*)") == "adamw"
+    assert profiling.short_name(UPD.replace("ElemBF16, 2", "ElemBF16, 5")) == "syrk"
+    assert profiling.short_name(UPD.replace("ElemBF16, 2", "ElemBF16, 4")) == "final_tall"
     assert profiling.short_name(COPY) == ""
 
 
