@@ -142,7 +142,8 @@ mfsdp_status_t mfsdp_muon_step(const mfsdp_matrix_t* mats, int64_t n_mats,
  * device fp32[n] read only; all 16-byte aligned and non-overlapping.
  * n == 0 (an owner with no tail) returns MFSDP_OK without touching the device.
  * Validation: non-null pointers for n > 0, n >= 0, step >= 1, finite
- * hyperparameters, beta1 and beta2 in [0, 1), eps >= 0.
+ * hyperparameters, beta1 and beta2 in [0, 1), eps >= 0; n > 2^40 returns
+ * MFSDP_ERR_UNSUPPORTED.
  */
 mfsdp_status_t mfsdp_adamw_tail(float* param, const float* grad,
                                 float* exp_avg, float* exp_avg_sq, int64_t n,

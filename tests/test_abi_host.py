@@ -183,6 +183,7 @@ def test_adamw_validation():
     assert call(lr=float("inf")) == 1
     assert call(g=None) == 1
     assert call(m=P + 8192 + 4) == 1            # misaligned
+    assert call(n=(1 << 40) + 4) == 2           # MFSDP_ERR_UNSUPPORTED, before any launch
     assert call(m=P + 8192) == 4                # overlaps g
     assert call(v=P + 100 * 16) == 4            # overlaps p
 
