@@ -344,29 +344,11 @@ hipError_t get_pool(StreamPool** out) {
   return hipSuccess;
 }
 
-// Workgroups of a Newton-Schulz launch over `ntiles` tiles: one per tile, or
-// (walk) one per CU, each walking its XCD's tiles in turn so that a tile's
-// epilogue overlaps the first DMA stages of the next.  Walking suits a launch
-// that has the GPU to itself; launches of concurrent stream groups keep one
-// workgroup per tile, so that the hardware can interleave them.
-template <class E, int MODE>
-unsigned ns_grid(int64_t ntiles, bool walk) {
-  return static_cast<unsigned>(walk && ns_walks<E, MODE>() ? std::min<int64_t>(ntiles, kCus)
-                                                           : ntiles);
-}
-
-// Whether single-stream calls walk tiles (default) or launch one workgroup
-// per tile: MFSDP_NS_WALK=0/1 overrides it (measurement).
-bool ns_walk(int groups) {
-  if (const char* env = getenv("MFSDP_NS_WALK")) return atoi(env) != 0 && groups == 1;
-  return groups == 1;
-}
-
 // Newton-Schulz iterations of one group on one stream.
 template <class E>
 hipError_t enqueue_ns_group(const Plan& p, const Plan::Group& gr, const MatDesc* descs,
                             const int2* tiles, const float* scales, float decay, int ns_steps,
-                            float a, float b, float c, bool walk, hipStream_t stream) {
+                            float a, float b, float c, hipStream_t stream) {
   const bool skip_poly = (c == 0.f);
   hipError_t e = hipSuccess;
   for (int it = 0; it < ns_steps; ++it) {
@@ -380,40 +362,38 @@ hipError_t enqueue_ns_group(const Plan& p, const Plan::Group& gr, const MatDesc*
     ep.c = c;
     ep.kb = skip_poly ? b : 1.f;
     ep.decay = decay;
-    ep.ntiles = static_cast<int>(gr.sym);
     e = launch(MFSDP_KERNEL_GRAM, stream, [&] {
-      ns_gemm_kernel<E, kModeGram><<<dim3(ns_grid<E, kModeGram>(gr.sym, walk)), dim3(kThreads), 0,
+      ns_gemm_kernel<E, kModeGram><<<dim3(static_cast<unsigned>(gr.sym)), dim3(kThreads), 0,
                                      stream>>>(descs, tiles + gr.t_sym, scales, ep);
     });
     if (e != hipSuccess) return e;
     if (!skip_poly) {
       e = launch(MFSDP_KERNEL_POLY, stream, [&] {
-        ns_gemm_kernel<E, kModePoly><<<dim3(ns_grid<E, kModePoly>(gr.sym, walk)), dim3(kThreads), 0,
+        ns_gemm_kernel<E, kModePoly><<<dim3(static_cast<unsigned>(gr.sym)), dim3(kThreads), 0,
                                        stream>>>(descs, tiles + gr.t_sym, scales, ep);
       });
       if (e != hipSuccess) return e;
     }
     if (it + 1 < ns_steps) {
-      ep.ntiles = static_cast<int>(gr.upd);
       e = launch(MFSDP_KERNEL_UPDATE, stream, [&] {
-        ns_gemm_kernel<E, kModeUpdate><<<dim3(ns_grid<E, kModeUpdate>(gr.upd, walk)), dim3(kThreads), 0,
+        ns_gemm_kernel<E, kModeUpdate><<<dim3(static_cast<unsigned>(gr.upd)), dim3(kThreads), 0,
                                          stream>>>(descs, tiles + gr.t_upd, scales, ep);
       });
       if (e != hipSuccess) return e;
     } else {
       if (gr.fin_wide > 0) {
-        ep.ntiles = static_cast<int>(gr.fin_wide);
         e = launch(MFSDP_KERNEL_FINAL, stream, [&] {
-          ns_gemm_kernel<E, kModeApplyWide><<<dim3(ns_grid<E, kModeApplyWide>(gr.fin_wide, walk)), dim3(kThreads), 0,
-                                              stream>>>(descs, tiles + gr.t_fin_wide, scales, ep);
+          ns_gemm_kernel<E, kModeApplyWide><<<dim3(static_cast<unsigned>(gr.fin_wide)),
+                                              dim3(kThreads), 0, stream>>>(
+              descs, tiles + gr.t_fin_wide, scales, ep);
         });
         if (e != hipSuccess) return e;
       }
       if (gr.fin_tall > 0) {
-        ep.ntiles = static_cast<int>(gr.fin_tall);
         e = launch(MFSDP_KERNEL_FINAL, stream, [&] {
-          ns_gemm_kernel<E, kModeApplyTall><<<dim3(ns_grid<E, kModeApplyTall>(gr.fin_tall, walk)), dim3(kThreads), 0,
-                                              stream>>>(descs, tiles + gr.t_fin_tall, scales, ep);
+          ns_gemm_kernel<E, kModeApplyTall><<<dim3(static_cast<unsigned>(gr.fin_tall)),
+                                              dim3(kThreads), 0, stream>>>(
+              descs, tiles + gr.t_fin_tall, scales, ep);
         });
         if (e != hipSuccess) return e;
       }
@@ -460,10 +440,9 @@ hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nest
   }
 
   const int ng = static_cast<int>(p.groups.size());
-  const bool walk = ns_walk(ng);
   if (ng == 1)
     return enqueue_ns_group<E>(p, p.groups[0], descs, tiles, scales, decay, ns_steps, a, b, c,
-                               walk, stream);
+                               stream);
 
   std::lock_guard<std::mutex> lock(g_pool_mu);
   StreamPool* pool = nullptr;
@@ -477,8 +456,7 @@ hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nest
   }
   for (int g = 0; g < ng; ++g) {
     hipStream_t s = g == 0 ? stream : pool->aux[g - 1];
-    e = enqueue_ns_group<E>(p, p.groups[g], descs, tiles, scales, decay, ns_steps, a, b, c, walk,
-                            s);
+    e = enqueue_ns_group<E>(p, p.groups[g], descs, tiles, scales, decay, ns_steps, a, b, c, s);
     if (e != hipSuccess) return e;
   }
   for (int g = 1; g < ng; ++g) {
@@ -581,7 +559,6 @@ hipError_t enqueue_stats(const StatsPlan& p, int64_t n, char* ws, float alpha, f
   ep.cur = 0;
   ep.a = alpha;
   ep.b = beta;
-  ep.ntiles = static_cast<int>(p.syrk_tiles);   // one workgroup per tile
   return launch(MFSDP_KERNEL_SYRK, stream, [&] {
     ns_gemm_kernel<E, kModeSyrk><<<dim3(static_cast<unsigned>(p.syrk_tiles)), dim3(kThreads), 0,
                                    stream>>>(syrk, reinterpret_cast<const int2*>(ws + p.off_tiles),

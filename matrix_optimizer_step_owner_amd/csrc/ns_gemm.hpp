@@ -76,7 +76,6 @@ struct NsEpi {
   int b_is_A;     // c == 0: the update multiplies A (scaled by kb = b)
   int fold;       // the poly stores B' = aI + bA + cA^2, so the update is
                   // X' = B'X with no read of X in its epilogue
-  int ntiles;     // tiles in the launch's table (see ns_gemm_kernel)
   float a, b, c;
   float kb;       // factor of the B X product in the update epilogue
   float decay;    // 1 - lr*wd
@@ -276,16 +275,6 @@ __host__ __device__ constexpr int dma_slot_piece(int sub, int idx) {
 // Tile rows per band of the update's tile order (see ns_gemm_kernel).
 constexpr int kUpdBandRows = 4;
 
-// Whether a kernel can walk several tiles per workgroup (see ns_gemm_kernel):
-// the bf16 update and apply kernels.  The symmetric products (with their
-// mirrored epilogue) and the fp32 kernels would run out of registers.  A
-// launch of any other kernel must have one workgroup per tile.
-template <class E, int MODE>
-__host__ __device__ constexpr bool ns_walks() {
-  return (MODE == kModeUpdate || MODE == kModeApplyWide || MODE == kModeApplyTall) &&
-         E::kVec == 8;
-}
-
 template <class E, int MODE>
 __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     const MatDesc* __restrict__ descs, const int2* __restrict__ tiles,
@@ -298,74 +287,49 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
 
   // Pipeline stages, each holding the P panel then the Q panel.  Separate
   // objects so that the compiler can tell a DMA into one stage from reads of
-  // another and does not serialize them.  The epilogue stages the
-  // accumulators in st3 and st4, so that the next tile's first three stages
-  // can be filled while it runs.
+  // another and does not serialize them.
   __shared__ uint4 st0[2 * PANEL];
   __shared__ uint4 st1[2 * PANEL];
   __shared__ uint4 st2[2 * PANEL];
   __shared__ uint4 st3[2 * PANEL];
-  __shared__ uint4 st4[2 * PANEL];
 
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int wr = wave >> 1, wc = wave & 1;
-
-  // Tiles of this workgroup.  The table holds ep.ntiles (matrix, tile)
-  // entries; XCD x (workgroups x, x + 8, ...) walks the contiguous range
-  // [t_begin, t_begin + t_count) of it, its workgroups t_step apart.  With
-  // one workgroup per tile (gridDim.x == ep.ntiles) each takes one tile; with
-  // fewer, each walks several and fills the next tile's first stages while
-  // the current tile's epilogue runs.
-  const int xcd = static_cast<int>(blockIdx.x) % kXcds;
-  const int wi = static_cast<int>(blockIdx.x) / kXcds;
-  const int tq = ep.ntiles / kXcds, tr = ep.ntiles % kXcds;
-  const int t_begin = xcd * tq + min(xcd, tr), t_count = tq + (xcd < tr ? 1 : 0);
-  const int t_step = static_cast<int>(gridDim.x) / kXcds +
-                     (xcd < static_cast<int>(gridDim.x) % kXcds ? 1 : 0);
-  if (wi >= t_count) return;   // uniform over the workgroup
+  const int tid = threadIdx.x;
+  // tiles[b] = (matrix, tile index within it) of logical tile b
+  const int2 tile = tiles[xcd_remap(blockIdx.x, gridDim.x)];
+  const int k = tile.x;
+  const int local = tile.y;
+  const MatDesc d = descs[k];
 
   constexpr bool kApply = MODE == kModeApplyWide || MODE == kModeApplyTall;
   constexpr bool kUpd = MODE == kModeUpdate || kApply;
-  constexpr bool kWalk = ns_walks<E, MODE>();
+  int ti, tj;
+  if (kUpd) {
+    // Bands of kUpdBandRows tile rows, walked column by column: the tiles an
+    // XCD runs together then share few operand panels (4 B' row panels and 8
+    // X column panels for 32 tiles, against 2 and 22 in row-major order),
+    // which cut the update time by 14% on the Llama-3-8B share.
+    const int tn = d.n_pad / kTile, tm = d.m_pad / kTile;
+    const int band = local / (kUpdBandRows * tn), r = local - band * (kUpdBandRows * tn);
+    const int rows = min(kUpdBandRows, tm - band * kUpdBandRows);
+    ti = band * kUpdBandRows + r % rows;
+    tj = r / rows;
+  } else {
+    upper_tile(local, d.m_pad / kTile, ti, tj);
+  }
+  const int row0 = ti * kTile, col0 = tj * kTile;
 
-  // Geometry of one tile: its matrix, tile row and column, and the operands.
-  struct Geo {
-    int k, ti, tj;
-    const S* P;
-    const S* Q;
-    int ldp, ldq, K;
-  };
-  auto geo_of = [&](int li) {
-    Geo g;
-    // tiles[b] = (matrix, tile index within it) of logical tile b
-    const int2 tile = tiles[t_begin + li];
-    g.k = tile.x;
-    const int local = tile.y;
-    const MatDesc& dd = descs[g.k];
-    if (kUpd) {
-      // Bands of kUpdBandRows tile rows, walked column by column: the tiles an
-      // XCD runs together then share few operand panels (4 B' row panels and 8
-      // X column panels for 32 tiles, against 2 and 22 in row-major order),
-      // which cut the update time by 14% on the Llama-3-8B share.
-      const int tn = dd.n_pad / kTile, tm = dd.m_pad / kTile;
-      const int band = local / (kUpdBandRows * tn), r = local - band * (kUpdBandRows * tn);
-      const int rows = min(kUpdBandRows, tm - band * kUpdBandRows);
-      g.ti = band * kUpdBandRows + r % rows;
-      g.tj = r / rows;
-    } else {
-      upper_tile(local, dd.m_pad / kTile, g.ti, g.tj);
-    }
-    const S* Xc = static_cast<const S*>(ep.cur ? dd.X1 : dd.X0);
-    if (MODE == kModeGram || MODE == kModeSyrk) {
-      g.P = Xc; g.Q = Xc; g.ldp = g.ldq = dd.n_pad; g.K = dd.n_pad;
-    } else if (MODE == kModePoly) {
-      g.P = static_cast<const S*>(dd.A); g.Q = g.P; g.ldp = g.ldq = dd.m_pad; g.K = dd.m_pad;
-    } else {
-      g.P = static_cast<const S*>(ep.b_is_A ? dd.A : dd.B); g.ldp = dd.m_pad;
-      g.Q = Xc; g.ldq = dd.n_pad; g.K = dd.m_pad;
-    }
-    return g;
-  };
+  const S* Xcur = static_cast<const S*>(ep.cur ? d.X1 : d.X0);
+  const S* P;
+  const S* Q;
+  int ldp, ldq, K;
+  if (MODE == kModeGram || MODE == kModeSyrk) {
+    P = Xcur; Q = Xcur; ldp = ldq = d.n_pad; K = d.n_pad;
+  } else if (MODE == kModePoly) {
+    P = static_cast<const S*>(d.A); Q = P; ldp = ldq = d.m_pad; K = d.m_pad;
+  } else {
+    P = static_cast<const S*>(ep.b_is_A ? d.A : d.B); ldp = d.m_pad;
+    Q = Xcur; ldq = d.n_pad; K = d.m_pad;
+  }
 
   // ---- operand panels: global -> LDS by DMA ---------------------------------
   // Each wave issues global_load_lds_dwordx4: lane l's 16 bytes land at
@@ -374,88 +338,48 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   // chunk c of row r stored at r*4 + (c ^ kswz(r)).  The K-strided panel of
   // the update (X, bf16): 32 k-rows x 32 chunks (256 columns), chunk c of row k
   // at k*32 + (c ^ 4*(k & 3)); fp32: 16 k-rows x 64 chunks, unswizzled.
-  //
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+
   // DMA piece q (0..7) of one K step: pieces 0..3 fill the P panel, 4..7 the
   // Q panel; each piece is one 1 KB wave instruction.  The per-lane byte
-  // offset of a piece is fixed for the whole K loop of a tile; only the
-  // uniform base moves with k0 (SGPR base + constant VGPR offset, no address
-  // VALU).
-  // (The lane index is made opaque so that none of this is hoisted out of
-  // the tile loop and kept live across it.)
-  auto make_doff = [&](const Geo& g, uint32_t (&doff)[8]) {
-    int lane = static_cast<int>(threadIdx.x) & 63;
-    if constexpr (kWalk) asm volatile("" : "+v"(lane));
-    const int r0p = g.ti * kTile, c0q = g.tj * kTile;
+  // offset of a piece is fixed for the whole K loop; only the uniform base
+  // moves with k0 (SGPR base + constant VGPR offset, no address VALU).
+  uint32_t doff[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int u = wave * 256 + (q & 3) * 64 + lane;
-      if (q < 4 || !kUpd) {
-        const int ld = q < 4 ? g.ldp : g.ldq;
-        const int r0 = q < 4 ? r0p : c0q;
-        const int row = u >> 2, c = (u & 3) ^ kswz(row);
-        doff[q] = static_cast<uint32_t>((static_cast<size_t>(r0 + row) * ld + c * V) * sizeof(S));
-      } else {
-        constexpr int UPR = kTile / V;    // 16-byte chunks per k-row
-        const int kk = u / UPR, pc = u % UPR;
-        const int c = (V == 8) ? (pc ^ (4 * (kk & 3))) : pc;
-        doff[q] = static_cast<uint32_t>((static_cast<size_t>(kk) * g.ldq + c0q + c * V) * sizeof(S));
-      }
+  for (int q = 0; q < 8; ++q) {
+    const int u = wave * 256 + (q & 3) * 64 + lane;
+    if (q < 4 || !kUpd) {
+      const int ld = q < 4 ? ldp : ldq;
+      const int r0 = q < 4 ? row0 : col0;
+      const int row = u >> 2, c = (u & 3) ^ kswz(row);
+      doff[q] = static_cast<uint32_t>((static_cast<size_t>(r0 + row) * ld + c * V) * sizeof(S));
+    } else {
+      constexpr int UPR = kTile / V;    // 16-byte chunks per k-row
+      const int kk = u / UPR, pc = u % UPR;
+      const int c = (V == 8) ? (pc ^ (4 * (kk & 3))) : pc;
+      doff[q] = static_cast<uint32_t>((static_cast<size_t>(kk) * ldq + col0 + c * V) * sizeof(S));
     }
-  };
+  }
   // Every DMA destination is a link-time constant (the stage object and the
   // piece) plus this wave's uniform offset: no per-lane address work.
   const uint32_t wave_off = static_cast<uint32_t>(wave) * 4096u;
-  auto dma_piece_of = [&](auto stage_c, const Geo& g, const uint32_t (&doff)[8], int k0, int q) {
+  auto dma_piece = [&](auto stage_c, int k0, int q) {
     constexpr int stage = decltype(stage_c)::value;
     const uint4* sbuf = stage == 0 ? st0 : stage == 1 ? st1 : stage == 2 ? st2 : st3;
     const char* base;
     if (q < 4)
-      base = reinterpret_cast<const char*>(g.P + k0);
+      base = reinterpret_cast<const char*>(P + k0);
     else if (!kUpd)
-      base = reinterpret_cast<const char*>(g.Q + k0);
+      base = reinterpret_cast<const char*>(Q + k0);
     else
-      base = reinterpret_cast<const char*>(g.Q + static_cast<size_t>(k0) * g.ldq);
+      base = reinterpret_cast<const char*>(Q + static_cast<size_t>(k0) * ldq);
     const uint32_t dst = lds_addr(sbuf) + wave_off + (q < 4 ? 0u : PANEL * 16u) +
                          static_cast<uint32_t>(q & 3) * 1024u;
     lds_dma16(dst, doff[q], base);
   };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-  // steps 0..2 of a tile into stages 0..2
-  auto prologue = [&](const Geo& g, const uint32_t (&doff)[8]) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) dma_piece_of(S0{}, g, doff, 0, q);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) dma_piece_of(S1{}, g, doff, BK, q);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) dma_piece_of(S2{}, g, doff, 2 * BK, q);
-  };
-
-  int li = wi;
-  Geo g = geo_of(li);
-  uint32_t doff[8];
-  make_doff(g, doff);
-  prologue(g, doff);
-  // wait for step 0 (steps 1 and 2 may stay in flight)
-  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  for (;;) {
-  // Per-lane indices, recomputed for every tile from an opaque copy of the
-  // thread index: address arithmetic hoisted out of the tile loop would stay
-  // live in registers across it and spill.
-  int tid = static_cast<int>(threadIdx.x);
-  if constexpr (kWalk) asm volatile("" : "+v"(tid));
-  const int lane = tid & 63;
-  const int lrow = lane & 31, lhalf = lane >> 5;
-  const int k = g.k;
-  const MatDesc d = descs[k];
-  const int ti = g.ti, tj = g.tj;
-  const int row0 = ti * kTile, col0 = tj * kTile;
-  const S* Xcur = static_cast<const S*>(ep.cur ? d.X1 : d.X0);
-  const int K = g.K;
-  auto dma_piece = [&](auto stage_c, int k0, int q) { dma_piece_of(stage_c, g, doff, k0, q); };
 
   // ---- fragments --------------------------------------------------------------
   // Lane l holds, for K sub-step s (0, 1), the 16-byte K-slice 2s + l/32
@@ -562,8 +486,19 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   // ---- main loop: four stages, unrolled by four ----------------------------
   using yes = std::integral_constant<bool, true>;
   using no = std::integral_constant<bool, false>;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
   const int nk = K / BK;                // multiple of 8: K is a multiple of 256
-  // stage 0 of this tile has landed (see the waits that precede the body)
+  // prologue: steps 0..2 in flight, wait for step 0
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_piece(S0{}, 0, q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_piece(S1{}, BK, q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_piece(S2{}, 2 * BK, q);
+  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int p = 0; p < kReadPieces; ++p) read_piece(st0, 0, p, fa[0], fb[0]);
   int t = 0;
@@ -580,20 +515,6 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   kstep(st3, S2{}, st0, 0, no{}, no{}, yes{});
   __syncthreads();
 
-  // Every wave has finished reading the stages: start the next tile's first
-  // three steps now, so that they land while this tile's epilogue runs.
-  // (Its DMA offsets are recomputed after the epilogue rather than kept live
-  // through it.)
-  const int li_next = li + t_step;
-  const bool more = kWalk && li_next < t_count;
-  Geo gn = g;
-  if (more) {
-    gn = geo_of(li_next);
-    uint32_t doff_n[8];
-    make_doff(gn, doff_n);
-    prologue(gn, doff_n);
-  }
-
   // ---- epilogue through LDS -------------------------------------------------
   // acc[i][j][r] sits at tile row wr*128 + i*32 + (r/4)*8 + lhalf*4 + r%4,
   // tile column wc*128 + j*32 + lrow.  For each i, the four waves stage their
@@ -606,9 +527,9 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   constexpr int SP = 128;               // staged row pitch in floats
   // column c of staged row r lives at r*SP + (c ^ 4*((r >> 2) & 7))
   auto sidx = [](int r, int c) { return r * SP + (c ^ (((r >> 2) & 7) << 2)); };
-  // wave slice w lives in half w & 1 (16 KB) of st3 (w < 2) or st4
+  // wave slice w lives in stage array w (16 KB of its 32 KB)
   auto slice_of = [&](int w) -> float* {
-    return reinterpret_cast<float*>(w < 2 ? st3 : st4) + (w & 1) * (kTile * 16);
+    return reinterpret_cast<float*>(w == 0 ? st0 : w == 1 ? st1 : w == 2 ? st2 : st3);
   };
   const float s_norm = scales[k];
   constexpr bool sym = !kUpd;
@@ -767,16 +688,6 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   block(std::integral_constant<int, 1>{});
   block(std::integral_constant<int, 2>{});
   block(std::integral_constant<int, 3>{});
-
-  if (!more) break;
-  // The epilogue's last barrier has ordered its reads of st3 before the next
-  // K loop's DMA into it; wait until the next tile's three stages have landed
-  // (the epilogue's stores are counted too: wait for everything).
-  li = li_next;
-  g = gn;
-  make_doff(g, doff);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
 }
 
 }  // namespace mfsdp
