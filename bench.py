@@ -390,6 +390,10 @@ def main():
             e["tflops"] = round(flops[k] / (v["avg_ms"] * 1e-3) / 1e12, 2)
         if k in ew:
             e["gbs"] = round(ew[k] / (v["avg_ms"] * 1e-3) / 1e9, 1)
+        if k == "final":
+            # the last update (2 m^2 n per matrix) split over the wide-matrix and
+            # tall-matrix launches: per step, not per launch
+            e["tflops_per_step"] = round(flops["update"] / (v["ms_per_step"] * 1e-3) / 1e12, 2)
         kernels[k] = e
 
     out = {
