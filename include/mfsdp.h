@@ -119,6 +119,16 @@ mfsdp_status_t mfsdp_muon_workspace_size(const mfsdp_matrix_t* mats,
  * workspace        device, >= mfsdp_muon_workspace_size bytes, 256-byte
  *                  aligned; contents are scratch and are overwritten.
  * n_mats == 0      (a rank that owns no matrix) returns MFSDP_OK, no work.
+ * Streams: when a list has few rounds of tiles, the Newton-Schulz iterations
+ * run as up to four flop-balanced groups of matrices.  The first group runs on
+ * `stream`; the others run on auxiliary streams that the library owns, one
+ * set per device, created on first use at the default priority and kept until
+ * the process ends.  The auxiliary streams are forked from `stream` with an
+ * event and joined back into it before the call returns, so all the work is
+ * ordered after earlier work on `stream` and before later work on it.  The
+ * environment variable MFSDP_NS_GROUPS=1 keeps everything on `stream`.
+ * Calls may come from several host threads; the stream pool is guarded by a
+ * mutex.
  * Validation: non-null weight/grad/momentum, rows, cols >= 1, 16-byte
  * aligned buffers, pairwise non-overlapping weight/grad/momentum/update_out/
  * workspace across the whole list, ns_steps in [0, 100], finite lr, beta,
