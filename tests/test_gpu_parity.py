@@ -225,6 +225,34 @@ def test_stream_group_count_is_bitwise_invariant(monkeypatch):
             assert torch.equal(st.M[i], ref.M[i]), (groups, i)
 
 
+def test_caller_stream_orders_every_group():
+    # The whole d=2048 block (two stream groups) on a non-default caller
+    # stream: copies of W and M made on that stream right after the call
+    # see the finished step, bitwise equal to the same step on the default
+    # stream, so both groups were joined back into the caller's stream.
+    inp = wlm.generate("block_d2048", seed=0)
+    hp = muon_hparams(inp.workload)
+    dev = torch.device("cuda:0")
+
+    def run(side):
+        W = [t.to(dev) for t in inp.weights]
+        G = [t.to(dev) for t in inp.grads]
+        M = [t.to(dev) for t in inp.momenta]
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream(device=dev) if side else torch.cuda.current_stream(dev)
+        with torch.cuda.stream(s):
+            mf.muon_step(W, G, M, **hp)
+            out = [t.clone() for t in W + M]
+        torch.cuda.synchronize()
+        return out
+
+    ref = run(False)
+    got = run(True)
+    say(f"caller stream: {len(got)} tensors compared")
+    for i, (a, b) in enumerate(zip(ref, got)):
+        assert torch.equal(a, b), i
+
+
 def test_resume_equals_continuous():
     Ws, Gs, Ms = _subset_inputs()
     hp = muon_hparams()
