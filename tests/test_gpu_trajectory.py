@@ -97,6 +97,27 @@ def test_bf16_trajectory_10_steps():
         assert max(ems) <= BF16_TOL, (t + 1, ems)
 
 
+def test_bf16_trajectory_block_d2048_3_steps():
+    # The d=2048 block at its real shapes and launch configuration (two
+    # Newton-Schulz stream groups), three consecutive steps, same bars.
+    shapes = [(s.rows, s.cols) for s in wlm.WORKLOADS["block_d2048"].matrices]
+    T = 3
+    W0, gpu, ref = run_trajectory(shapes, torch.bfloat16, T, seed=400)
+    for t in range(T):
+        ratios, ems = [], []
+        for k in range(len(shapes)):
+            Wr, Wg = ref[t][0][k], gpu[t][0][k]
+            err = np.linalg.norm(Wg - Wr)
+            allow = (BF16_TOL * np.linalg.norm(Wr - W0[k])
+                     + 0.5 * math.sqrt(t + 1) * np.linalg.norm(ulp_bf16(Wr)))
+            ratios.append(err / allow)
+            ems.append(rel(gpu[t][1][k], ref[t][1][k]))
+        say(f"d=2048 block bf16 step {t + 1}: W error / allowance {max(ratios):.3f}, "
+            f"rel(M_t) {max(ems):.2e}")
+        assert max(ratios) <= 1.0, (t + 1, ratios)
+        assert max(ems) <= BF16_TOL, (t + 1, ems)
+
+
 def test_adamw_trajectory_20_steps():
     n, T = 4099, 20
     p0, _, m0, v0 = wlm.random_tail_state(n, seed=300)
