@@ -8,8 +8,9 @@
  * on one data-parallel owner and every other rank holds an empty shard for it;
  * after the ordinary gradient reduction the owner holds the whole gradient, so
  * its Muon step -- momentum, Newton-Schulz orthogonalization of the whole
- * matrix, update -- involves no communication.  Non-matrix tensors are packed
- * into tail owners and keep AdamW.  This library is that step on one GPU:
+ * matrix, update -- involves no communication.  Tensors that are not 2D
+ * matrices are gathered on tail owners and updated there with AdamW.  This
+ * library is that step on one GPU:
  *
  *   mfsdp_muon_step   -- Muon on the owner's list of whole matrices,
  *   mfsdp_adamw_tail  -- AdamW on a packed fp32 tail buffer.
@@ -142,7 +143,8 @@ mfsdp_status_t mfsdp_muon_step(const mfsdp_matrix_t* mats, int64_t n_mats,
 
 /*
  * Decoupled AdamW on a packed fp32 tail of n elements (arxivlens Abstract:
- * non-matrix tensors are packed into tail owners and stay on AdamW).
+ * the tensors that are not 2D matrices go to tail owners in packed form and
+ * keep the AdamW optimizer).
  * Elementwise, with t = step (>= 1):
  *   p  <- p * (1 - lr*weight_decay)
  *   m  <- beta1*m + (1-beta1)*g
@@ -164,7 +166,7 @@ mfsdp_status_t mfsdp_adamw_tail(float* param, const float* grad,
 /*
  * Balance-aware owner planner (host only; touches no device).
  *
- * Source: arxivlens page, Summary (a balance-aware owner planner assigns
+ * Source: arxivlens page, Methodology (a balance-aware owner planner assigns
  * ownership by bytes and by work); gist.science summaries, "Méthodologie",
  * part 2, first mechanism (a global planner chooses owners so that resident
  * bytes and optimizer work are balanced across the ranks).  The pages give no
@@ -197,8 +199,8 @@ mfsdp_status_t mfsdp_plan_owners(const double* cost_ms, const int64_t* bytes,
 
 /*
  * Packed tail layout (host only).  Source: arxivlens Abstract and gist.science
- * "Méthodologie", part 1: non-matrix tensors are packed into a tail owner,
- * which runs AdamW on the packed buffer.
+ * "Méthodologie", part 1: vectors and other non-2D tensors go, grouped, to a
+ * tail owner, which runs AdamW on the packed buffer.
  * Tensor i of numel[i] fp32 elements occupies elements
  * [offsets[i], offsets[i] + numel[i]) of the packed buffer; segments follow
  * in order, each starting on a 16-byte (4-element) boundary.  *total is the
@@ -240,10 +242,10 @@ mfsdp_status_t mfsdp_tail_unpack(const float* packed, int64_t packed_numel,
 /*
  * Preconditioner statistics of Shampoo-type matrix optimizers on the owner.
  *
- * Source: arxivlens page, Abstract and Key takeaways, and gist.science
- * summaries, "Contributions clés": the owner-shaped layout serves matrix
- * optimizers in general (Shampoo and SOAP as well as Muon), since each needs
- * the whole 2D gradient on one rank.  The pages give no formulas; the
+ * Source: gist.science summaries (French and Portuguese pages),
+ * "Problématique" (Shampoo and SOAP, like Muon, take the whole 2D gradient
+ * as input) and "Contributions clés", item "Généralité" (the owner-shaped
+ * layout is not tied to one optimizer).  The arxivlens page names only Muon.  The pages give no formulas; the
  * statistics are the textbook Shampoo ones (Gupta, Koren and Singer 2018),
  * with SOAP's exponential moving average as the beta/alpha form.
  *

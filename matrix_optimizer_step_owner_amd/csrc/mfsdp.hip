@@ -3,9 +3,10 @@
 //
 // Source of the operations: "MatrixFSDP: communication-free matrix optimizers
 // under ZeRO-3 parameter sharding" (arxivlens page, Abstract): the owner of a
-// whole 2D weight runs Muon's Newton-Schulz on it locally, and non-matrix
-// tensors packed into tail owners take AdamW.  One call covers the owner's
-// whole list: every kernel is one grouped launch over all owned matrices.
+// whole 2D weight runs Muon's Newton-Schulz on it locally, and the tensors
+// that are not 2D matrices, gathered in packed form on tail owners, take
+// AdamW.  One call covers the owner's whole list: every kernel is one grouped
+// launch over all owned matrices.
 
 #include <hip/hip_runtime.h>
 

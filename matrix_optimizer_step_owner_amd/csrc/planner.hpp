@@ -1,11 +1,11 @@
 // Host-side owner planner, packed-tail layout and launch tile order.
 //
 // Source: "MatrixFSDP: communication-free matrix optimizers under ZeRO-3
-// parameter sharding" -- arxivlens page, Summary (a balance-aware owner
+// parameter sharding" -- arxivlens page, Methodology (a balance-aware owner
 // planner assigns ownership by bytes and by work); gist.science summaries,
 // "Méthodologie", part 2, first mechanism (a global planner picks owners so
 // that resident bytes and optimizer work are balanced across the ranks), and
-// part 1 (non-matrix tensors are packed into a tail owner).
+// part 1 (1D and other non-2D tensors are grouped on a separate tail owner).
 //
 // The pages give no algorithm.  This planner is greedy longest-processing-
 // time-first scheduling (Graham, 1969) with a per-owner byte cap: whole items

@@ -1,10 +1,10 @@
 """Balance-aware owner planning for a model's optimizer state.
 
 Source: "MatrixFSDP: communication-free matrix optimizers under ZeRO-3
-parameter sharding" -- arxivlens page, Summary (ownership assigned by a
+parameter sharding" -- arxivlens page, Methodology (ownership assigned by a
 balance-aware planner, by bytes and by work); gist.science summaries,
 "Méthodologie", part 2, first mechanism (resident bytes and optimizer work
-balanced across the ranks), part 1 (non-matrix tensors packed into a tail
+balanced across the ranks), part 1 (1D and other non-2D tensors grouped on a tail
 owner).
 
 Every 2D weight is an item owned whole by one rank; every non-matrix tensor

@@ -14,7 +14,8 @@ part 1 "Owner-shaped placement"):
 * every 2D weight lives whole on one owner, whose optimizer step runs Muon on
   the whole matrix -- a momentum-smoothed update orthogonalized by a
   Newton-Schulz iteration -- with no communication;
-* non-matrix tensors are packed into tail owners and take an AdamW step.
+* every tensor that is not a 2D matrix goes, packed, to a tail owner, where
+  AdamW updates it.
 
 The pages give no formula for either step, so each arithmetic choice is a
 reading stated in the docstring where it is made.  The oracle is written in

@@ -5,8 +5,8 @@ import this module.
 
 Source: "MatrixFSDP: communication-free matrix optimizers under ZeRO-3
 parameter sharding" (arxivlens page), Abstract, and the gist.science summaries
-("Méthodologie", part 1): 1D and other non-matrix tensors are packed into tail
-owners and keep the ordinary AdamW optimizer.  The pages give no formula;
+("Méthodologie", part 1): vectors and the other tensors that are not 2D go,
+grouped in one buffer, to tail owners and keep the ordinary AdamW optimizer.  The pages give no formula;
 reading R11 takes textbook decoupled AdamW (Loshchilov & Hutter): weight decay
 multiplies the parameter, moments are exponential averages, both are
 bias-corrected with the step count t (t = 1 on the first step), and eps is

@@ -4,10 +4,10 @@ TEST INFRASTRUCTURE ONLY -- see the package docstring.  No product code may
 import this module.
 
 Source: "MatrixFSDP: communication-free matrix optimizers under ZeRO-3
-parameter sharding" -- arxivlens page, Summary (ownership is assigned by a
+parameter sharding" -- arxivlens page, Methodology (ownership is assigned by a
 balance-aware planner, by bytes and by work); gist.science summaries,
 "Méthodologie", part 2, first mechanism (resident bytes and optimizer work
-balanced across ranks) and part 1 (non-matrix tensors packed into a tail
+balanced across ranks) and part 1 (1D and other non-2D tensors grouped on a tail
 owner).  The pages give no algorithm.  Reading R20: greedy
 longest-processing-time-first (Graham 1969) under a per-owner byte cap, with
 the tie rules written below; tails packed in order with 16-byte aligned

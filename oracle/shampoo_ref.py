@@ -4,10 +4,11 @@ TEST INFRASTRUCTURE ONLY -- see the package docstring.  No product code may
 import this module.
 
 Source: "MatrixFSDP: communication-free matrix optimizers under ZeRO-3
-parameter sharding" -- arxivlens page (Abstract, Key takeaways) and the
-gist.science summaries ("Contributions clés"): the owner-shaped layout serves
-matrix optimizers in general, Shampoo and SOAP as well as Muon, because each
-needs the whole 2D gradient on one rank.  The pages give no formulas.
+parameter sharding" -- gist.science summaries (French and Portuguese pages),
+"Problématique" (Shampoo and SOAP, like Muon, take the whole 2D gradient as
+input) and "Contributions clés", item "Généralité" (the owner-shaped layout is
+not tied to one optimizer: Muon, Shampoo and SOAP all run on it).  The arxivlens
+page names only Muon.  The pages give no formulas.
 Reading R21: the textbook Shampoo statistics (Gupta, Koren and Singer 2018),
 L += G G^T and R += G^T G, with SOAP's moving-average form
 L <- beta L + alpha G G^T (alpha = 1 - beta) as the general case.

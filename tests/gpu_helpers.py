@@ -1,13 +1,7 @@
 """Helpers shared by the GPU parity tests: run the HIP step, run the oracle on
-the same host values, and compare with the acceptance bars.
-
-Acceptance (relative Frobenius error, float64, per tensor):
-  * bf16 path: O and M' within 2e-2; W' within
-        ||W'_gpu - W'_ref||_F <= 2e-2 ||W'_ref - W||_F + 0.5 ||ulp_bf16(W'_ref)||_F
-    (an update is only a few bf16 ulps of W, so the final rounding of W' is
-    allowed for separately);
-  * fp32 path: O, M' and W' - W within 1e-4;
-  * AdamW: p', m', v' within 1e-6.
+the same host values, and compare with the acceptance bars of
+tests/parity_checks.py (per tensor, per 256 x 256 tile, and elementwise for
+the momentum).
 """
 
 from __future__ import annotations
@@ -21,38 +15,13 @@ import torch
 import matrix_optimizer_step_owner_amd as mf
 import oracle
 
-BF16_TOL = 2e-2
-F32_TOL = 1e-4
-ADAMW_TOL = 1e-6
+from parity_checks import (ADAMW_TOL, BF16_TOL, F32_TOL, compare_matrix, rel,  # noqa: F401
+                           ulp_bf16, w_error_bf16)
 
 
 def say(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
-
-
-def rel(x, y) -> float:
-    x = np.asarray(x, dtype=np.float64)
-    y = np.asarray(y, dtype=np.float64)
-    den = np.linalg.norm(y)
-    num = np.linalg.norm(x - y)
-    if den == 0.0:
-        return 0.0 if num == 0.0 else float("inf")
-    return float(num / den)
-
-
-def ulp_bf16(x: np.ndarray) -> np.ndarray:
-    ax = np.abs(x)
-    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
-    e = np.maximum(e, -126)
-    return np.where(ax > 0, np.exp2(e - 7), np.exp2(-133.0))
-
-
-def w_error_bf16(W_gpu, W_ref, W0) -> float:
-    """Ratio of the W' error to its allowance (<= 1 passes)."""
-    err = np.linalg.norm(np.asarray(W_gpu, np.float64) - W_ref)
-    allow = BF16_TOL * np.linalg.norm(W_ref - W0) + 0.5 * np.linalg.norm(ulp_bf16(W_ref))
-    return float(err / allow)
 
 
 def f64(t: torch.Tensor) -> np.ndarray:
@@ -94,22 +63,16 @@ def oracle_matrix(W, G, M, hp, scale=None):
                                    ns_steps=hp["ns_steps"], abc=hp["abc"], scale=scale)
 
 
-def check_matrix(idx, W0, Wg, Mg, Og, ref, dtype, label=""):
-    """Compare one matrix's GPU results with the oracle's; returns errors."""
-    W_ref, M_ref, O_ref = ref
-    e_o = rel(Og, O_ref) if Og is not None else 0.0
-    e_m = rel(Mg, M_ref)
-    if dtype == torch.bfloat16:
-        e_w = w_error_bf16(Wg, W_ref, W0)
-        ok = e_o <= BF16_TOL and e_m <= BF16_TOL and e_w <= 1.0
-    else:
-        e_w = rel(np.asarray(Wg) - W0, W_ref - W0)
-        ok = e_o <= F32_TOL and e_m <= F32_TOL and e_w <= F32_TOL
-    msg = f"{label} matrix {idx} {tuple(W0.shape)}: rel O={e_o:.3e} M={e_m:.3e} W={e_w:.3e}"
+def check_matrix(idx, W0, G, M0, Wg, Mg, Og, ref, dtype, beta, label=""):
+    """Compare one matrix's GPU results with the oracle's (every bar of
+    parity_checks.compare_matrix); returns (rel O, rel M', W' figure)."""
+    ok, f = compare_matrix(W0, G, M0, Wg, Mg, Og, ref, beta, dtype == torch.bfloat16)
+    msg = (f"{label} matrix {idx} {tuple(W0.shape)}: rel O={f['O']:.3e} M={f['M']:.3e} "
+           f"W={f['W']:.3e}; worst tile O={f['O_tile']:.3e} at {f['O_tile_at']}, "
+           f"W={f['W_tile']:.3e} at {f['W_tile_at']}; M' worst {f['M_ulp']:.2f} ulp")
     say(msg)
-    assert np.isfinite(e_o) and np.isfinite(e_m) and np.isfinite(e_w), msg
     assert ok, msg
-    return e_o, e_m, e_w
+    return f["O"], f["M"], f["W"]
 
 
 def run_and_check(weights, grads, momenta, hp, dtype, label="", scales=None,
@@ -124,6 +87,6 @@ def run_and_check(weights, grads, momenta, hp, dtype, label="", scales=None,
     for i in idxs:
         s = None if scales is None else scales[i]
         ref = oracle_matrix(weights[i], grads[i], momenta[i], hp, scale=s)
-        out.append(check_matrix(i, W0[i], f64(st.W[i]), f64(st.M[i]), f64(st.U[i]), ref,
-                                dtype, label))
+        out.append(check_matrix(i, W0[i], f64(grads[i]), f64(momenta[i]), f64(st.W[i]),
+                                f64(st.M[i]), f64(st.U[i]), ref, dtype, hp["beta"], label))
     return st, out

@@ -287,3 +287,35 @@ def test_prepared_step_object_equals_function():
     torch.cuda.synchronize()
     for i in range(len(Ws)):
         assert torch.equal(a.W[i], b.W[i]) and torch.equal(a.M[i], b.M[i]), i
+
+
+@pytest.mark.parametrize("groups", ["1", "2"])
+def test_nan_gradient_stays_in_its_matrix(monkeypatch, groups):
+    # Non-finite inputs propagate and nothing checks them, but matrices are
+    # independent: a NaN in one matrix's gradient must leave every other
+    # matrix of the same grouped call bitwise equal to a clean run, on one
+    # stream and with two Newton-Schulz stream groups.  In the poisoned
+    # matrix, M' differs from the clean M' only at the NaN element, and its
+    # norm (hence every NS iterate, O and W') is NaN.
+    monkeypatch.setenv("MFSDP_NS_GROUPS", groups)
+    Ws, Gs, Ms = _subset_inputs()
+    hp = muon_hparams()
+    clean = GpuStep(Ws, Gs, Ms)
+    clean.run(**hp)
+    k, (r, c) = 1, (700, 33)
+    Gbad = [g.clone() for g in Gs]
+    Gbad[k][r, c] = float("nan")
+    bad = GpuStep(Ws, Gbad, Ms)
+    bad.run(**hp)
+    for i in range(len(Ws)):
+        if i == k:
+            continue
+        assert torch.equal(bad.W[i], clean.W[i]) and torch.equal(bad.M[i], clean.M[i]), i
+        assert torch.equal(bad.U[i], clean.U[i]), i
+    nan_m = torch.isnan(bad.M[k])
+    assert nan_m.sum().item() == 1 and nan_m[r, c].item()
+    keep = ~nan_m
+    assert torch.equal(bad.M[k][keep], clean.M[k][keep])
+    assert torch.isnan(bad.U[k]).all().item() and torch.isnan(bad.W[k]).all().item()
+    say(f"NaN in matrix {k} ({tuple(Ws[k].shape)}), groups={groups}: "
+        f"{len(Ws) - 1} other matrices bitwise clean")

@@ -2,6 +2,8 @@
 
 * round_to_bf16: torch's float32 -> bfloat16 conversion (round to nearest,
   ties to even) on many float32 values, and hand-worked ties;
+* round_to_f32: torch's float64 -> float32 conversion on many float64 values,
+  exact float32 midpoints and their neighbours, and hand-worked ties;
 * muon_trajectory: one step equals the single-step oracle; with float64
   state the carried momentum has the closed form
   M_T = beta^T M_0 + sum_k beta^(T-1-k) G_k;
@@ -42,6 +44,33 @@ def test_round_to_bf16_matches_torch_on_float32_values():
 ])
 def test_round_to_bf16_hand_cases(x, want):
     assert oracle.round_to_bf16(np.array([x]))[0] == want
+
+
+def test_round_to_f32_matches_torch_on_float64_values():
+    # float64 values over a wide exponent range, plus the exact midpoints
+    # between neighbouring float32 values (ties: to even) and points one
+    # float64 ulp either side of them
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(200_000) * np.exp(rng.uniform(-60, 60, 200_000))
+    f = x[:2000].astype(np.float32)
+    nxt = np.nextafter(f, np.float32(np.inf), dtype=np.float32)
+    mids = (f.astype(np.float64) + nxt.astype(np.float64)) / 2.0
+    x = np.concatenate([x, mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf)])
+    want = torch.from_numpy(x).to(torch.float32).double().numpy()
+    got = oracle.round_to_f32(x)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("x,want", [
+    (1.0 + 2.0 ** -24, 1.0),                          # tie, rounds to even (down)
+    (1.0 + 3 * 2.0 ** -24, 1.0 + 2.0 ** -22),         # tie, rounds to even (up)
+    (-(1.0 + 2.0 ** -24), -1.0),
+    (1.0 + 2.0 ** -24 + 2.0 ** -50, 1.0 + 2.0 ** -23),  # just above the tie
+    (0.1, 0.100000001490116119384765625),             # nearest float32 to 0.1
+    (0.0, 0.0),
+])
+def test_round_to_f32_hand_cases(x, want):
+    assert oracle.round_to_f32(np.array([x]))[0] == want
 
 
 def _mats(seed, shapes):

@@ -5,6 +5,8 @@ Pins of the reference (oracle.planner_ref):
   {7,3,2} / {5,4,3}, makespan 12 = total / 2 (optimal);
 * Graham's bound: the LPT makespan is within (4/3 - 1/(3R)) of the optimum,
   the optimum found by trying every assignment of small instances;
+* the byte cap and a schedule that the cap changes, worked by hand, and the
+  rule for an item that no owner can take under the cap;
 * tail layout offsets worked by hand.
 The library must then give exactly the reference's assignment (same greedy
 rule and tie breaks) on random instances, with and without a binding byte cap.
@@ -26,6 +28,37 @@ def test_hand_worked_schedule():
     assert owner == [0, 1, 1, 0, 1, 0] and load == [12.0, 12.0]
     assert ref.optimal_makespan(cost, 2) == 12.0
     assert mf.plan_owners(cost, [1] * 6, 2, byte_slack=10.0) == (owner, load, used)
+
+
+def test_byte_cap_hand_worked():
+    # cap = ceil((1 + slack) * max(total / R, largest item))
+    assert ref.byte_cap([1, 10, 10, 1], 2, 0.0) == 11
+    assert ref.byte_cap([3, 4], 2, 0.5) == 6          # largest item binds: 4 * 1.5
+    assert ref.byte_cap([5, 5, 5], 2, 0.1) == 9       # ceil(7.5 * 1.1 = 8.25)
+
+
+def test_binding_cap_changes_the_schedule():
+    # costs 6,5,4,3 with bytes 1,10,10,1 on two owners, cap 11 (worked by hand):
+    #   6 -> owner 0 (tie, lower rank)     loads 6,0   bytes 1,0
+    #   5 -> owner 1 (less loaded)         loads 6,5   bytes 1,10
+    #   4 -> owner 1 would hold 20 > 11: owner 0       loads 10,5  bytes 11,10
+    #   3 -> owner 0 would hold 12 > 11: owner 1       loads 10,8  bytes 11,11
+    cost, nbytes = [6, 5, 4, 3], [1, 10, 10, 1]
+    want = ([0, 1, 0, 1], [10.0, 8.0], [11, 11])
+    assert ref.lpt_owners(cost, nbytes, 2, 0.0) == want
+    assert mf.plan_owners(cost, nbytes, 2, byte_slack=0.0) == want
+    # without a binding cap LPT puts both 10-byte items on owner 1
+    assert ref.lpt_owners(cost, nbytes, 2, 10.0) == ([0, 1, 1, 0], [9.0, 9.0], [2, 20])
+
+
+def test_no_owner_under_the_cap_goes_to_fewest_bytes():
+    # three 10-byte items on two owners, cap ceil(max(15, 10)) = 15:
+    #   3 -> owner 0; 2 -> owner 1 (owner 0 would hold 20);
+    #   1 -> neither stays under 15: the owner with the fewest bytes, tie 10/10
+    #        to the lower rank, owner 0
+    want = ([0, 1, 0], [4.0, 2.0], [20, 10])
+    assert ref.lpt_owners([3, 2, 1], [10, 10, 10], 2, 0.0) == want
+    assert mf.plan_owners([3, 2, 1], [10, 10, 10], 2, byte_slack=0.0) == want
 
 
 @pytest.mark.parametrize("seed", range(12))
