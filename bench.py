@@ -76,8 +76,20 @@ def elementwise_bytes(shapes, es, tail_n):
             "adamw": tail_n * 7 * 4}         # read p, g, m, v; write p, m, v
 
 
-def cpu_baseline(key, budget_s=20.0):
-    """Time the float64 oracle on a bounded sample of the workload."""
+def cpu_sample_order(wl):
+    """Matrix indices in order of increasing Newton-Schulz work (the oracle's
+    bounded sample takes them smallest first)."""
+    return sorted(range(len(wl.matrices)),
+                  key=lambda i: ns_flops_by_kind([(wl.matrices[i].rows,
+                                                   wl.matrices[i].cols)])["update"])
+
+
+def cpu_baseline(key, sample, budget_s=20.0):
+    """Time the float64 oracle on a bounded sample of the workload.
+
+    ``sample`` is a list of (index, W, G, M) host tensors, smallest first, taken
+    from the bench's own inputs; matrices are stepped until ``budget_s`` of
+    oracle time is spent."""
     import oracle
     from matrix_optimizer_step_owner_amd import workloads as wlm
     try:
@@ -86,18 +98,11 @@ def cpu_baseline(key, budget_s=20.0):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     wl = wlm.WORKLOADS[key]
-    # smallest-first distinct shapes until the budget is spent
-    order = sorted(range(len(wl.matrices)),
-                   key=lambda i: ns_flops_by_kind([(wl.matrices[i].rows,
-                                                    wl.matrices[i].cols)])["update"])
-    inp = wlm.generate(key, seed=0, matrix_indices=order[:8])
-    idx_map = {i: k for k, i in enumerate(sorted(order[:8]))}
     done_flops = 0
     done = []
     t_total = 0.0
-    for i in order[:8]:
-        k = idx_map[i]
-        W, G, M = (t.double().numpy() for t in (inp.weights[k], inp.grads[k], inp.momenta[k]))
+    for i, Wt, Gt, Mt in sample:
+        W, G, M = (t.double().numpy() for t in (Wt, Gt, Mt))
         t0 = time.perf_counter()
         oracle.muon_matrix_step(W, G, M, lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov,
                                 weight_decay=wl.weight_decay, ns_steps=wl.ns_steps,
@@ -105,7 +110,7 @@ def cpu_baseline(key, budget_s=20.0):
         t_total += time.perf_counter() - t0
         f = ns_flops_by_kind([(wl.matrices[i].rows, wl.matrices[i].cols)])
         done_flops += wl.ns_steps * sum(f.values())
-        done.append(f"{wl.matrices[i].rows}x{wl.matrices[i].cols}")
+        done.append(f"{wl.matrices[i].name} {wl.matrices[i].rows}x{wl.matrices[i].cols}")
         if t_total > budget_s:
             break
     return {"value": done_flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads,
@@ -240,7 +245,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="block_d2048")
+    ap.add_argument("--workload", default="d5120_2blocks",
+                    help="workload key (default: the 32B-class d=5120 two-block share, "
+                         "the largest owner share that fits one GPU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -284,13 +291,20 @@ def main():
     if args.shampoo_stats:
         stats_bench(args, wl, dev)
         return
+    t_setup = time.perf_counter()
     inp = wlm.generate(args.workload, seed=0)
+    setup_gen_s = time.perf_counter() - t_setup
     shapes = [(s.rows, s.cols) for s in wl.matrices]
+    # host copies of the oracle's sample (smallest matrices first)
+    sample = [] if args.no_cpu_baseline else [
+        (i, inp.weights[i], inp.grads[i], inp.momenta[i]) for i in cpu_sample_order(wl)[:8]]
     W = [t.to(dev) for t in inp.weights]
     G = [t.to(dev) for t in inp.grads]
     M = [t.to(dev) for t in inp.momenta]
     P, Gt, Mt, Vt = (t.to(dev) for t in (inp.tail_p, inp.tail_g, inp.tail_m, inp.tail_v))
     del inp
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
     es = 2 if wl.dtype == torch.bfloat16 else 4
     ws = torch.empty(mf.muon_workspace_size(shapes, wl.dtype), dtype=torch.uint8, device=dev)
     hp = dict(lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov, weight_decay=wl.weight_decay,
@@ -420,7 +434,8 @@ def main():
         "cold_cache": {"reps": len(cold), "flush_bytes": FLUSH_BYTES,
                        "ms_median": round(cold[len(cold) // 2], 4), "ms_min": round(cold[0], 4)},
         "roofline": roof,
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.workload,
+        "setup_s": {"generate": round(setup_gen_s, 1), "generate_and_upload": round(setup_s, 1)},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.workload, sample,
                                                                       args.cpu_budget),
     }
     print(json.dumps(out), flush=True)

@@ -19,8 +19,8 @@
  *   - Every pointer named "device" is a device (HBM) address on the current
  *     HIP device.  The caller owns every buffer; the library never allocates
  *     or frees device memory.  Host pointers are read only during the call.
- *   - Work is enqueued asynchronously on `stream`; no call synchronizes the
- *     host with the device.
+ *   - Work is enqueued asynchronously on `stream`; no call waits for device
+ *     work to finish.
  *   - All arguments are validated before anything is enqueued.  On any
  *     status other than MFSDP_OK nothing has been modified, except for
  *     MFSDP_ERR_HIP, which is returned when the HIP runtime fails after work
@@ -123,13 +123,21 @@ mfsdp_status_t mfsdp_muon_workspace_size(const mfsdp_matrix_t* mats,
  * Streams: when a list has few rounds of tiles, the Newton-Schulz iterations
  * run as up to four flop-balanced groups of matrices.  The first group runs on
  * `stream`; the others run on auxiliary streams that the library owns, one
- * set per device, created on first use at the default priority and kept until
- * the process ends.  The auxiliary streams are forked from `stream` with an
- * event and joined back into it before the call returns, so all the work is
- * ordered after earlier work on `stream` and before later work on it.  The
- * environment variable MFSDP_NS_GROUPS=1 keeps everything on `stream`.
- * Calls may come from several host threads; the stream pool is guarded by a
- * mutex.
+ * set per (device, caller stream), created on first use at the default
+ * priority and kept until the process ends.  The auxiliary streams are forked
+ * from `stream` with an event and joined back into it before the call
+ * returns, so all the work is ordered after earlier work on `stream` and
+ * before later work on it; calls on different caller streams share no
+ * auxiliary stream.  The environment variable MFSDP_NS_GROUPS=1 keeps
+ * everything on `stream`.  Calls may come from several host threads (one
+ * caller stream per thread at a time); the pool lookup is guarded by a mutex.
+ * Launch tables: each call uploads its descriptors and tile tables into the
+ * workspace with hipMemcpyAsync from host memory that lives only during the
+ * call (the HIP runtime stages such a copy before it returns).  A stream that
+ * is being captured into a graph is therefore refused with
+ * MFSDP_ERR_UNSUPPORTED, before anything is enqueued.
+ * MFSDP_LOG=1 prints each call's launch plan (groups, tiles per launch,
+ * padded shapes, workspace bytes) to stderr.
  * Validation: non-null weight/grad/momentum, rows, cols >= 1, 16-byte
  * aligned buffers, pairwise non-overlapping weight/grad/momentum/update_out/
  * workspace across the whole list, ns_steps in [0, 100], finite lr, beta,
@@ -274,7 +282,9 @@ mfsdp_status_t mfsdp_stats_workspace_size(const mfsdp_stats_matrix_t* mats,
                                           size_t* out_bytes);
 
 /* Statistics update over the list, enqueued on `stream`.  workspace: device,
- * >= mfsdp_stats_workspace_size bytes, 256-byte aligned, scratch.
+ * >= mfsdp_stats_workspace_size bytes, 256-byte aligned, scratch.  Like
+ * mfsdp_muon_step, the call uploads its launch tables from host memory and
+ * refuses a stream under graph capture (MFSDP_ERR_UNSUPPORTED).
  * Validation before any launch: rows, cols >= 1; non-null grad and left;
  * naturally aligned buffers; grad/left/right/workspace pairwise disjoint
  * across the list (MFSDP_ERR_ALIAS); finite beta and alpha. */

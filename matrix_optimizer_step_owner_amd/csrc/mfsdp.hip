@@ -17,8 +17,10 @@
 #include <cstring>
 #include <exception>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/mfsdp.h"
@@ -312,9 +314,13 @@ mfsdp_status_t check_aliasing(std::vector<Range>& rs) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Per-device pool of auxiliary streams and fork/join events for the
-// Newton-Schulz groups.  Created on first use, kept until the process ends
-// (host objects; no device memory).  Every stream has the default priority.
+// Auxiliary streams and fork/join events for the Newton-Schulz groups, one
+// set per (device, caller stream): calls on different caller streams never
+// share an auxiliary stream, so they do not wait for each other's groups.
+// Created on first use and kept until the process ends (host objects, no
+// device memory).  Every stream has the default priority.  A destroyed
+// caller stream whose handle is reused by a new stream reuses its set, which
+// is harmless: the set only orders work behind its current caller stream.
 struct StreamPool {
   hipStream_t aux[kMaxGroups - 1] = {};
   hipEvent_t fork = nullptr;
@@ -322,27 +328,74 @@ struct StreamPool {
 };
 
 std::mutex g_pool_mu;
-std::map<int, StreamPool> g_pools;
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<StreamPool>> g_pools;
 
-hipError_t get_pool(StreamPool** out) {
+hipError_t get_pool(hipStream_t caller, StreamPool** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  auto it = g_pools.find(dev);
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  auto key = std::make_pair(dev, caller);
+  auto it = g_pools.find(key);
   if (it == g_pools.end()) {
-    StreamPool sp;
+    std::unique_ptr<StreamPool> sp(new StreamPool);
     for (int i = 0; i < kMaxGroups - 1; ++i) {
-      e = hipStreamCreateWithFlags(&sp.aux[i], hipStreamNonBlocking);
+      e = hipStreamCreateWithFlags(&sp->aux[i], hipStreamNonBlocking);
       if (e != hipSuccess) return e;
-      e = hipEventCreateWithFlags(&sp.join[i], hipEventDisableTiming);
+      e = hipEventCreateWithFlags(&sp->join[i], hipEventDisableTiming);
       if (e != hipSuccess) return e;
     }
-    e = hipEventCreateWithFlags(&sp.fork, hipEventDisableTiming);
+    e = hipEventCreateWithFlags(&sp->fork, hipEventDisableTiming);
     if (e != hipSuccess) return e;
-    it = g_pools.emplace(dev, sp).first;
+    it = g_pools.emplace(key, std::move(sp)).first;
   }
-  *out = &it->second;
+  *out = it->second.get();
   return hipSuccess;
+}
+
+// The step and statistics calls upload their launch tables with a copy from
+// host memory that is freed when the call returns; a graph captured around
+// such a copy would replay a dangling host pointer.  Capture is refused
+// (before anything is enqueued, so the capture itself stays valid).
+mfsdp_status_t refuse_capture(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess)
+    return fail(MFSDP_ERR_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(MFSDP_ERR_UNSUPPORTED,
+                "the stream is being captured into a graph; the call uploads its launch "
+                "tables from host memory and cannot be captured");
+  return MFSDP_OK;
+}
+
+// MFSDP_LOG=1: print the launch plan of a step to stderr (debugging aid).
+bool log_enabled() {
+  const char* v = getenv("MFSDP_LOG");
+  return v && v[0] == '1';
+}
+
+void log_plan(const Plan& p, int64_t n, mfsdp_dtype_t dt, int ns_steps, hipStream_t stream) {
+  fprintf(stderr,
+          "mfsdp_muon_step: %lld matrices, %s, ns_steps %d, stream %p, workspace %zu bytes, "
+          "momentum blocks %lld, %zu Newton-Schulz group(s)\n",
+          (long long)n, dt == MFSDP_DTYPE_BF16 ? "bf16" : "fp32", ns_steps,
+          static_cast<void*>(stream), p.total, (long long)p.ew_total, p.groups.size());
+  for (size_t g = 0; g < p.groups.size(); ++g) {
+    const Plan::Group& gr = p.groups[g];
+    std::map<std::pair<int64_t, int64_t>, int> shapes;   // (m_pad, n_pad) -> count
+    for (int64_t i : gr.mats) shapes[{p.geom[i].m_pad, p.geom[i].n_pad}] += 1;
+    fprintf(stderr,
+            "  group %zu on %s: %zu matrices; tiles per launch: gram/poly %lld, update %lld, "
+            "final wide %lld, final tall %lld; padded shapes (m x n):",
+            g, g == 0 ? "the caller's stream" : "an auxiliary stream", gr.mats.size(),
+            (long long)gr.sym, (long long)gr.upd, (long long)gr.fin_wide,
+            (long long)gr.fin_tall);
+    for (const auto& kv : shapes)
+      fprintf(stderr, " %lldx%lld*%d", (long long)kv.first.first, (long long)kv.first.second,
+              kv.second);
+    fprintf(stderr, "\n");
+  }
 }
 
 // Newton-Schulz iterations of one group on one stream.
@@ -445,9 +498,8 @@ hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nest
     return enqueue_ns_group<E>(p, p.groups[0], descs, tiles, scales, decay, ns_steps, a, b, c,
                                stream);
 
-  std::lock_guard<std::mutex> lock(g_pool_mu);
   StreamPool* pool = nullptr;
-  e = get_pool(&pool);
+  e = get_pool(stream, &pool);
   if (e != hipSuccess) return e;
   e = hipEventRecord(pool->fork, stream);
   if (e != hipSuccess) return e;
@@ -653,6 +705,8 @@ mfsdp_status_t stats_impl(const mfsdp_stats_matrix_t* mats, int64_t n, mfsdp_dty
         },
         tab);
   }
+  st = refuse_capture(stream);
+  if (st != MFSDP_OK) return st;
   hipError_t e = hipMemcpyAsync(ws, blob.data(), p.blob_bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "descriptor upload: %s", hipGetErrorString(e));
   e = dtype == MFSDP_DTYPE_BF16 ? enqueue_stats<ElemBF16>(p, n, ws, alpha, beta, stream)
@@ -861,6 +915,10 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
       launch_order(tall, k_mm, all_tiles, tab + gr.t_fin_tall);
     }
   }
+
+  st = refuse_capture(stream);
+  if (st != MFSDP_OK) return st;
+  if (log_enabled()) log_plan(p, n_mats, dtype, ns_steps, stream);
 
   hipError_t e = hipMemcpyAsync(ws, blob.data(), p.blob_bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "descriptor upload: %s", hipGetErrorString(e));

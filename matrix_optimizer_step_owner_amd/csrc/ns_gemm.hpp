@@ -246,31 +246,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ int kswz(int row) { return (row >> 2) & 3; }
 
 // Which DMA piece (0..7, or -1 for none) a K step issues in MFMA slot idx of
-// sub-step sub: the eight 1 KB pieces of a stage are spread over the step so
-// that the vector-memory queue never holds up the MFMA issue for long.  The
-// default (2) issues one piece every fourth slot of both sub-steps: the four
-// waves of a CU share one texture addresser, which the bunched schedules (0:
-// the first eight slots of sub-step 0; 1: every other slot of sub-step 0)
-// keep busy long enough to stall MFMA issue (3% slower on the d=2048 block).
-#ifndef MFSDP_DMA_SCHED
-#define MFSDP_DMA_SCHED 2
-#endif
+// sub-step sub: the eight 1 KB pieces of a stage are spread over the step,
+// one every fourth MFMA slot of both sub-steps, so that the vector-memory
+// queue never holds up the MFMA issue for long.  The four waves of a CU share
+// one texture addresser: issuing a step's pieces in a burst (the first eight
+// slots of sub-step 0) kept it busy long enough to stall MFMA issue and was 3%
+// slower on the d=2048 block.
 __host__ __device__ constexpr int dma_slot_piece(int sub, int idx) {
-#if MFSDP_DMA_SCHED == 0
-  return (sub == 0 && idx < 8) ? idx : -1;
-#elif MFSDP_DMA_SCHED == 1
-  return (sub == 0 && (idx & 1) == 0) ? idx / 2 : -1;
-#else
   return (idx & 3) == 0 ? 4 * sub + idx / 4 : -1;
-#endif
 }
-// DMAs that may stay in flight at the barrier of step t: those of step t - 1
-// and the ones step t issued before its barrier (step t + 1's must be done).
-#if MFSDP_DMA_SCHED == 2
+// DMAs that may stay in flight at the barrier of step t: the eight of step
+// t - 1 and the four that step t issued before its barrier (step t + 1's must
+// be done).
 #define MFSDP_VM_IN_FLIGHT "12"
-#else
-#define MFSDP_VM_IN_FLIGHT "16"
-#endif
 
 // Tile rows per band of the update's tile order (see ns_gemm_kernel).
 constexpr int kUpdBandRows = 4;

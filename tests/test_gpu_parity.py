@@ -319,3 +319,80 @@ def test_nan_gradient_stays_in_its_matrix(monkeypatch, groups):
     assert torch.isnan(bad.U[k]).all().item() and torch.isnan(bad.W[k]).all().item()
     say(f"NaN in matrix {k} ({tuple(Ws[k].shape)}), groups={groups}: "
         f"{len(Ws) - 1} other matrices bitwise clean")
+
+
+def test_two_caller_streams_run_independently():
+    # Two lists on two caller streams, enqueued alternately so that their
+    # Newton-Schulz groups overlap on the GPU: each caller stream has its own
+    # auxiliary streams, and each result is bitwise equal to the same list
+    # stepped alone on the default stream.
+    dev = torch.device("cuda:0")
+    A = wlm.random_matrix_inputs([(512, 1536), (1536, 512), (1024, 1024), (300, 700)],
+                                 torch.bfloat16, seed=11)
+    B = wlm.random_matrix_inputs([(2048, 2048), (768, 256), (256, 2304)],
+                                 torch.bfloat16, seed=12)
+    hp = muon_hparams()
+
+    def dev_copy(lists):
+        return [[t.to(dev) for t in ts] for ts in lists]
+
+    refs = []
+    for lists in (A, B):
+        W, G, M = dev_copy(lists)
+        for _ in range(2):
+            mf.muon_step(W, G, M, **hp)
+        torch.cuda.synchronize()
+        refs.append((W, M))
+    (Wa, Ga, Ma), (Wb, Gb, Mb) = dev_copy(A), dev_copy(B)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    for _ in range(2):
+        with torch.cuda.stream(s1):
+            mf.muon_step(Wa, Ga, Ma, **hp)
+        with torch.cuda.stream(s2):
+            mf.muon_step(Wb, Gb, Mb, **hp)
+    torch.cuda.synchronize()
+    for (W, M), (Wr, Mr) in zip(((Wa, Ma), (Wb, Mb)), refs):
+        for i in range(len(W)):
+            assert torch.equal(W[i], Wr[i]) and torch.equal(M[i], Mr[i]), i
+    say("two caller streams: both lists bitwise equal to their default-stream runs")
+
+
+def test_graph_capture_is_refused():
+    # The step uploads its launch tables from host memory that is freed when
+    # the call returns, so a captured copy would replay a dangling pointer:
+    # the library refuses a capturing stream before enqueueing anything, and
+    # the capture around it stays valid.
+    dev = torch.device("cuda:0")
+    Ws, Gs, Ms = wlm.random_matrix_inputs([(256, 512)], torch.bfloat16, seed=13)
+    W, G, M = (t[0].to(dev) for t in (Ws, Gs, Ms))
+    ws = torch.empty(mf.muon_workspace_size([(256, 512)], torch.bfloat16), dtype=torch.uint8,
+                     device=dev)
+    W0 = W.clone()
+    x = torch.zeros(1024, device=dev)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        x.add_(1.0)
+        with pytest.raises(mf.MfsdpError) as err:
+            mf.muon_step([W], [G], [M], lr=0.02, workspace=ws)
+        g.capture_end()
+    assert err.value.status == 2          # MFSDP_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.equal(W, W0)
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+    assert torch.all(x == 3.0).item()
+    say(f"graph capture refused: {err.value}")
+
+
+def test_launch_plan_log(monkeypatch, capfd):
+    monkeypatch.setenv("MFSDP_LOG", "1")
+    Ws, Gs, Ms = _subset_inputs()
+    GpuStep(Ws, Gs, Ms).run(**muon_hparams())
+    err = capfd.readouterr().err
+    assert "mfsdp_muon_step: 5 matrices, bf16, ns_steps 5" in err, err
+    assert "group 0 on the caller's stream" in err and "2048x2048*1" in err, err
