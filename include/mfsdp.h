@@ -150,6 +150,36 @@ mfsdp_status_t mfsdp_muon_step(const mfsdp_matrix_t* mats, int64_t n_mats,
                                size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The same step for callers that cannot allocate device memory: code that
+ * may not call hipMalloc (tight serving loops, harnesses that forbid it, a
+ * caller with no free HBM left to hand out a workspace).  It takes the
+ * arguments of mfsdp_muon_step except the workspace, and uses instead a
+ * static device array of MFSDP_NOALLOC_SCRATCH_BYTES (256 MiB) that the
+ * library holds on every GPU it runs on, from the loading of its code object
+ * on that GPU until the process ends.
+ *   - A list whose workspace (mfsdp_muon_workspace_size) exceeds
+ *     MFSDP_NOALLOC_SCRATCH_BYTES is refused with MFSDP_ERR_WORKSPACE before
+ *     the device is touched: split the list, or use mfsdp_muon_step.
+ *   - The call allocates no device or pinned host memory and creates no
+ *     stream or event: every Newton-Schulz group runs on `stream` (results
+ *     are bitwise those of mfsdp_muon_step, which does not depend on the
+ *     grouping).  The only allocations are the host-side launch tables.
+ *   - All calls on one GPU share that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero: each call writes
+ *     what it reads).  Calls that overlap on one GPU -- on two streams, or
+ *     from two threads -- race on it and give undefined results; order them
+ *     on one stream.
+ *   - Like mfsdp_muon_step, a stream under graph capture is refused.
+ * Validation and every other error are those of mfsdp_muon_step.
+ */
+#define MFSDP_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+mfsdp_status_t mfsdp_muon_step_noalloc(const mfsdp_matrix_t* mats, int64_t n_mats,
+                                       mfsdp_dtype_t dtype, float lr, float beta,
+                                       int nesterov, float weight_decay, int ns_steps,
+                                       float a, float b, float c, hipStream_t stream);
+
+/*
  * Decoupled AdamW on a packed fp32 tail of n elements (arxivlens Abstract:
  * the tensors that are not 2D matrices go to tail owners in packed form and
  * keep the AdamW optimizer).

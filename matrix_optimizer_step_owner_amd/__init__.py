@@ -21,11 +21,12 @@ from typing import Dict, Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import MfsdpError, NS_EPS
+from ._lib import MfsdpError, NOALLOC_SCRATCH_BYTES, NS_EPS
 
-__all__ = ["muon_step", "MuonStep", "adamw_tail", "muon_workspace_size", "default_scale",
-           "plan_owners", "tail_layout", "tail_pack", "tail_unpack", "shampoo_stats",
-           "timing", "MfsdpError", "NS_EPS", "library_path"]
+__all__ = ["muon_step", "muon_step_noalloc", "MuonStep", "adamw_tail", "muon_workspace_size",
+           "default_scale", "plan_owners", "tail_layout", "tail_pack", "tail_unpack",
+           "shampoo_stats", "timing", "MfsdpError", "NS_EPS", "NOALLOC_SCRATCH_BYTES",
+           "library_path"]
 
 library_path = _lib.LIB_PATH
 
@@ -151,6 +152,50 @@ def muon_step(weights: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
                                    workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(),
                                    stream))
+
+
+def muon_step_noalloc(weights: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
+                      momenta: Sequence[torch.Tensor], *, lr: float, beta: float = 0.95,
+                      nesterov: bool = True, weight_decay: float = 0.0,
+                      ns_steps: int = 5, abc=(3.4445, -4.7750, 2.0315),
+                      scales: Optional[Sequence[float]] = None,
+                      update_out: Optional[Sequence[torch.Tensor]] = None) -> None:
+    """Owner-local Muon step with the library's static device scratch as its
+    workspace (mfsdp_muon_step_noalloc): no device memory is allocated, by the
+    library or here.  Lists needing more than NOALLOC_SCRATCH_BYTES of
+    workspace are refused; calls that overlap on one GPU race on the shared
+    scratch.  Same arguments and results as ``muon_step``."""
+    lib = _lib.load()
+    n = len(weights)
+    if not (len(grads) == n and len(momenta) == n):
+        raise ValueError("weights, grads and momenta must have the same length")
+    if scales is not None and len(scales) != n:
+        raise ValueError("scales must have one entry per matrix")
+    if update_out is not None and len(update_out) != n:
+        raise ValueError("update_out must have one entry per matrix")
+    if n == 0:
+        return
+    dtype = weights[0].dtype
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    device = weights[0].device
+    if device.type != "cuda":
+        raise ValueError("muon_step_noalloc needs GPU tensors")
+    for i in range(n):
+        if weights[i].dim() != 2:
+            raise ValueError(f"weights[{i}] must be 2D")
+        _check_matrix(weights[i], f"weights[{i}]", dtype, device)
+        _check_matrix(grads[i], f"grads[{i}]", dtype, device, weights[i].shape)
+        _check_matrix(momenta[i], f"momenta[{i}]", dtype, device, weights[i].shape)
+        if update_out is not None and update_out[i] is not None:
+            _check_matrix(update_out[i], f"update_out[{i}]", torch.float32, device,
+                          weights[i].shape)
+    arr = _build_descs(weights, grads, momenta, scales, update_out)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    a, b, c = abc
+    _lib.check(lib.mfsdp_muon_step_noalloc(arr, n, _DTYPES[dtype], lr, beta,
+                                           1 if nesterov else 0, weight_decay, ns_steps,
+                                           a, b, c, stream))
 
 
 class MuonStep:

@@ -16,11 +16,14 @@ STATUS_NAMES = {0: "MFSDP_OK", 1: "MFSDP_ERR_INVALID_ARGUMENT",
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 NS_EPS = 1e-7
+#: size of the static device scratch of mfsdp_muon_step_noalloc (bytes)
+NOALLOC_SCRATCH_BYTES = 256 << 20
 KERNEL_KINDS = {"momentum": 0, "norm": 1, "gram": 2, "poly": 3, "update": 4,
                 "apply": 5, "adamw": 6, "final": 7, "stats_prep": 8, "syrk": 9}
 
 #: Every symbol include/mfsdp.h declares.
-EXPORTED = ("mfsdp_muon_workspace_size", "mfsdp_muon_step", "mfsdp_adamw_tail",
+EXPORTED = ("mfsdp_muon_workspace_size", "mfsdp_muon_step", "mfsdp_muon_step_noalloc",
+            "mfsdp_adamw_tail",
             "mfsdp_plan_owners", "mfsdp_tail_layout", "mfsdp_tail_pack",
             "mfsdp_tail_unpack", "mfsdp_stats_workspace_size", "mfsdp_shampoo_stats",
             "mfsdp_status_string", "mfsdp_last_error",
@@ -77,6 +80,10 @@ def load() -> ctypes.CDLL:
             c.c_int, c.c_float, c.c_int, c.c_float, c.c_float, c.c_float,
             c.c_void_p, c.c_size_t, c.c_void_p]
         lib.mfsdp_muon_step.restype = c.c_int
+        lib.mfsdp_muon_step_noalloc.argtypes = [
+            c.POINTER(MfsdpMatrix), c.c_int64, c.c_int, c.c_float, c.c_float,
+            c.c_int, c.c_float, c.c_int, c.c_float, c.c_float, c.c_float, c.c_void_p]
+        lib.mfsdp_muon_step_noalloc.restype = c.c_int
         lib.mfsdp_adamw_tail.argtypes = [
             c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64,
             c.c_float, c.c_float, c.c_float, c.c_float, c.c_float, c.c_int64,

@@ -174,7 +174,7 @@ constexpr int kMaxGroups = 4;
 // Number of Newton-Schulz groups for a call: one when a single grouped launch
 // already has many rounds of tiles, more when few rounds would leave CUs idle
 // at the end of each launch.  MFSDP_NS_GROUPS overrides it (debugging).
-int choose_groups(int64_t n, int64_t upd_total) {
+int choose_groups(int64_t n, int64_t upd_total, int max_groups) {
   int g;
   const int64_t rounds = upd_total / kCus;
   if (upd_total < kCus / 4) g = 1;          // latency-bound; not worth streams
@@ -184,7 +184,7 @@ int choose_groups(int64_t n, int64_t upd_total) {
     const int v = atoi(env);
     if (v >= 1 && v <= kMaxGroups) g = v;
   }
-  return static_cast<int>(std::min<int64_t>(g, n));
+  return static_cast<int>(std::min<int64_t>(std::min(g, max_groups), n));
 }
 
 mfsdp_status_t make_geom(const mfsdp_matrix_t& mt, int64_t idx, MatGeom* g, size_t es) {
@@ -213,7 +213,8 @@ mfsdp_status_t make_geom(const mfsdp_matrix_t& mt, int64_t idx, MatGeom* g, size
   return MFSDP_OK;
 }
 
-mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t dt, Plan* p) {
+mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t dt, Plan* p,
+                          int max_groups = kMaxGroups) {
   const size_t es = elem_size(dt);
   p->geom.resize(n);
   for (int64_t i = 0; i < n; ++i) {
@@ -226,7 +227,7 @@ mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t d
   }
   // flop-balanced groups (largest first onto the least loaded group)
   {
-    const int ng = choose_groups(n, p->upd_total);
+    const int ng = choose_groups(n, p->upd_total, max_groups);
     p->groups.assign(ng, Plan::Group{});
     std::vector<int64_t> order(n), work(n);
     std::vector<int64_t> load(ng, 0);
@@ -786,7 +787,7 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
                                      mfsdp_dtype_t dtype, float lr, float beta, int nesterov,
                                      float weight_decay, int ns_steps, float a, float b,
                                      float c, void* workspace, size_t workspace_bytes,
-                                     hipStream_t stream) {
+                                     hipStream_t stream, int max_groups = kMaxGroups) {
   g_last_error.clear();
   if (dtype != MFSDP_DTYPE_F32 && dtype != MFSDP_DTYPE_BF16)
     return fail(MFSDP_ERR_UNSUPPORTED, "unsupported dtype %d", (int)dtype);
@@ -801,7 +802,7 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
   if (n_mats > (int64_t(1) << 20)) return fail(MFSDP_ERR_UNSUPPORTED, "too many matrices");
 
   Plan p;
-  mfsdp_status_t st = build_plan(mats, n_mats, dtype, &p);
+  mfsdp_status_t st = build_plan(mats, n_mats, dtype, &p, max_groups);
   if (st != MFSDP_OK) return st;
 
   const size_t es = elem_size(dtype);
@@ -991,6 +992,67 @@ static mfsdp_status_t adamw_tail_impl(float* param, const float* grad, float* ex
   return MFSDP_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Step without a caller workspace, for callers that cannot allocate device
+// memory: the workspace is a file-scope device array of fixed size, one copy
+// per GPU, which the loader places when the library's code object is loaded
+// on that GPU and which stays until the process ends.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MFSDP_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on each device, taken once per device with that
+// device current.  The host-side name `scratch` is only a stand-in: kernels
+// receive these addresses, never the name.
+static std::mutex g_scratch_mu;
+static std::map<int, void*> g_scratch_ptr;
+
+static mfsdp_status_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(MFSDP_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return MFSDP_OK;
+}
+
+// Same step as mfsdp_muon_step with the static scratch as its workspace.  The
+// size check comes first, before the device is touched.  Every Newton-Schulz
+// group stays on the caller's stream, so the call creates no auxiliary
+// stream or event.  Nothing in the workspace has to start at zero: the
+// momentum kernel writes every iterate's padding and each launch overwrites
+// the tables and partial sums it reads.
+static mfsdp_status_t muon_noalloc_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
+                                        mfsdp_dtype_t dtype, float lr, float beta,
+                                        int nesterov, float weight_decay, int ns_steps,
+                                        float a, float b, float c, hipStream_t stream) {
+  size_t need = 0;
+  mfsdp_status_t st = workspace_size_impl(mats, n_mats, dtype, &need);
+  if (st != MFSDP_OK) return st;
+  if (need > MFSDP_NOALLOC_SCRATCH_BYTES)
+    return fail(MFSDP_ERR_WORKSPACE,
+                "the list needs %zu bytes of workspace; the static scratch of "
+                "mfsdp_muon_step_noalloc holds %zu (MFSDP_NOALLOC_SCRATCH_BYTES): split the list "
+                "or call mfsdp_muon_step with a workspace",
+                need, static_cast<size_t>(MFSDP_NOALLOC_SCRATCH_BYTES));
+  if (n_mats == 0)   // validation of the hyperparameters, no device access
+    return muon_step_impl(mats, 0, dtype, lr, beta, nesterov, weight_decay, ns_steps, a, b, c,
+                          nullptr, 0, stream, 1);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MFSDP_OK) return st;
+  return muon_step_impl(mats, n_mats, dtype, lr, beta, nesterov, weight_decay, ns_steps, a, b,
+                        c, ws, MFSDP_NOALLOC_SCRATCH_BYTES, stream, 1);
+}
+
 // No C++ exception crosses the ABI: allocation failures of the host-side plan
 // become MFSDP_ERR_UNSUPPORTED.
 mfsdp_status_t mfsdp_muon_workspace_size(const mfsdp_matrix_t* mats, int64_t n_mats,
@@ -1009,6 +1071,18 @@ mfsdp_status_t mfsdp_muon_step(const mfsdp_matrix_t* mats, int64_t n_mats, mfsdp
   try {
     return muon_step_impl(mats, n_mats, dtype, lr, beta, nesterov, weight_decay, ns_steps, a, b,
                           c, workspace, workspace_bytes, stream);
+  } catch (const std::exception& ex) {
+    return fail(MFSDP_ERR_UNSUPPORTED, "host exception: %s", ex.what());
+  }
+}
+
+mfsdp_status_t mfsdp_muon_step_noalloc(const mfsdp_matrix_t* mats, int64_t n_mats,
+                                       mfsdp_dtype_t dtype, float lr, float beta, int nesterov,
+                                       float weight_decay, int ns_steps, float a, float b,
+                                       float c, hipStream_t stream) {
+  try {
+    return muon_noalloc_impl(mats, n_mats, dtype, lr, beta, nesterov, weight_decay, ns_steps,
+                             a, b, c, stream);
   } catch (const std::exception& ex) {
     return fail(MFSDP_ERR_UNSUPPORTED, "host exception: %s", ex.what());
   }

@@ -244,3 +244,20 @@ def test_fp32_iterate_byte_limit():
     assert st == 2
     st, nb = ws_size(arr, 1, _lib.DTYPE_BF16)
     assert st == 0 and nb > 0
+
+
+def test_noalloc_step_refuses_a_list_beyond_its_scratch():
+    # refused before the device is touched: the size check comes first
+    lib = _lib.load()
+    arr, _ = mats([(8192, 8192)])
+    assert ws_size(arr, 1)[1] > _lib.NOALLOC_SCRATCH_BYTES
+    abc = (3.4445, -4.775, 2.0315)
+    st = lib.mfsdp_muon_step_noalloc(arr, 1, _lib.DTYPE_BF16, 0.02, 0.95, 1, 0.01, 5, *abc,
+                                     None)
+    assert st == 3 and b"static scratch" in lib.mfsdp_last_error()
+    # an empty list is a no-op; its hyperparameters are still validated
+    assert lib.mfsdp_muon_step_noalloc(None, 0, _lib.DTYPE_BF16, 0.02, 0.95, 1, 0.01, 5,
+                                       *abc, None) == 0
+    assert lib.mfsdp_muon_step_noalloc(None, 0, _lib.DTYPE_BF16, float("nan"), 0.95, 1,
+                                       0.01, 5, *abc, None) == 1
+    assert lib.mfsdp_muon_step_noalloc(None, 0, 9, 0.02, 0.95, 1, 0.01, 5, *abc, None) == 2
