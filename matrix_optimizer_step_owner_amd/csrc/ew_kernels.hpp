@@ -10,9 +10,12 @@
 namespace mfsdp {
 
 // Momentum M' = beta*M + G, Nesterov U = G + beta*M' (or U = M'), sum of U^2
-// per tile, and U stored into X0 in wide layout (transposed when rows > cols),
-// zero in the tile padding.  One 256-thread workgroup per block of 64 stored
-// rows x 128 stored columns (kEwRows x kEwCols).
+// per block, and U stored into X0 in wide layout (transposed when rows > cols),
+// zero in the tile padding.  A block is 64 stored rows x 128 stored columns
+// (kEwRows x kEwCols) and owns one partial sum of U^2; one 256-thread
+// workgroup covers kEwSub consecutive blocks of one matrix, with every load of
+// all of them issued before the first store.  `wl` lists, per matrix, its
+// workgroups (ceil(blocks / kEwSub) of them).
 template <class E>
 __global__ __launch_bounds__(kThreads) void momentum_kernel(
     const MatDesc* __restrict__ descs, WorkList wl, double* __restrict__ partials,
@@ -20,13 +23,14 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
   using S = typename E::storage_t;
   constexpr int V = E::kVec;
   constexpr int SR = kEwRows, SC = kEwCols;
+  constexpr int SUB = kEwSub;
   // U staged in the storage type (values rounded as X0 stores them): 16.6 KB
-  // in bf16, so eight workgroups fit a CU.  Rows padded to 65 (bf16) or 129
-  // (fp32) 4-byte words: both the row-wise writes and the column-wise reads
-  // are free of bank conflicts.
+  // per block in bf16.  Rows padded to 65 (bf16) or 129 (fp32) 4-byte words:
+  // both the row-wise writes and the column-wise reads are free of bank
+  // conflicts.
   constexpr int kPad = 4 / static_cast<int>(sizeof(S));
-  __shared__ S sU[SR][SC + kPad];
-  __shared__ float sRed[kThreads / 64];
+  __shared__ S sU[SUB][SR][SC + kPad];
+  __shared__ float sRed[SUB][kThreads / 64];
   // 16 bytes of staged storage elements -> one vector
   auto pack_raw = [](const S (&w)[V]) -> uint4 {
     if constexpr (V == 8) {
@@ -43,120 +47,145 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
   const int bid = blockIdx.x;
   const int item = find_item(wl, bid);
   const MatDesc d = descs[wl.mat[item]];
-  const int local = bid - wl.begin[item];
-  const int ti = local / d.ew_tiles_j, tj = local % d.ew_tiles_j;
-  const int i0 = ti * d.ew_th, j0 = tj * d.ew_tw;   // wide tile origin
-  const int sr0 = d.tall ? j0 : i0;                  // stored-layout block origin
-  const int sc0 = d.tall ? i0 : j0;
+  const int first = (bid - wl.begin[item]) * SUB;   // first block of this workgroup
+  const int nsub = min(SUB, d.ew_ntiles - first);   // blocks it covers (>= 1)
   const int tid = threadIdx.x;
 
   const S* G = static_cast<const S*>(d.G);
   S* M = static_cast<S*>(d.M);
   S* X0 = static_cast<S*>(d.X0);
-  float ssq = 0.f;
+  float ssq[SUB];
+  int i0s[SUB], j0s[SUB];
+#pragma unroll
+  for (int q = 0; q < SUB; ++q) {
+    ssq[q] = 0.f;
+    const int local = first + min(q, nsub - 1);
+    const int ti = local / d.ew_tiles_j, tj = local % d.ew_tiles_j;
+    i0s[q] = ti * d.ew_th;   // wide block origin
+    j0s[q] = tj * d.ew_tw;
+  }
 
   if (d.vec_ok) {
     constexpr int VPR = SC / V;                 // vectors per stored row
-    constexpr int NV = SR * VPR / kThreads;     // vectors per thread
+    constexpr int NV = SR * VPR / kThreads;     // vectors per thread per block
     // All of this thread's loads first (the stores to M may alias G and M as
     // far as the compiler knows, so interleaving would serialize latency).
     // G, M' and U are streamed (non-temporal); M is loaded through the caches
     // because its line is written back in place.
-    uint4 graw[NV], mraw[NV];
+    uint4 graw[SUB][NV], mraw[SUB][NV];
 #pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int e = tid + it * kThreads;
-      const int r = e / VPR, cv = e % VPR;
-      const int sr = sr0 + r, sc = sc0 + cv * V;
-      if (sr < d.rows && sc < d.cols) {
-        const size_t off = static_cast<size_t>(sr) * d.cols + sc;
-        graw[it] = gld_stream(G + off);
-        mraw[it] = gld<uint4>(M + off);
+    for (int q = 0; q < SUB; ++q) {
+      const int sr0 = d.tall ? j0s[q] : i0s[q], sc0 = d.tall ? i0s[q] : j0s[q];
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int e = tid + it * kThreads;
+        const int sr = sr0 + e / VPR, sc = sc0 + (e % VPR) * V;
+        if (q < nsub && sr < d.rows && sc < d.cols) {
+          const size_t off = static_cast<size_t>(sr) * d.cols + sc;
+          graw[q][it] = gld_stream(G + off);
+          mraw[q][it] = gld<uint4>(M + off);
+        }
       }
     }
 #pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int e = tid + it * kThreads;
-      const int r = e / VPR, cv = e % VPR;
-      const int sr = sr0 + r, sc = sc0 + cv * V;
-      float u[V];
-      if (sr < d.rows && sc < d.cols) {
-        const size_t off = static_cast<size_t>(sr) * d.cols + sc;
-        float g[V], mo[V], mn[V];
-        Vec16<E>::unpack(graw[it], g);
-        Vec16<E>::unpack(mraw[it], mo);
+    for (int q = 0; q < SUB; ++q) {
+      if (q >= nsub) break;
+      const int sr0 = d.tall ? j0s[q] : i0s[q], sc0 = d.tall ? i0s[q] : j0s[q];
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-          mn[k] = fmaf(beta, mo[k], g[k]);
-          u[k] = nesterov ? fmaf(beta, mn[k], g[k]) : mn[k];
-          ssq = fmaf(u[k], u[k], ssq);
+      for (int it = 0; it < NV; ++it) {
+        const int e = tid + it * kThreads;
+        const int r = e / VPR, cv = e % VPR;
+        const int sr = sr0 + r, sc = sc0 + cv * V;
+        float u[V];
+        if (sr < d.rows && sc < d.cols) {
+          const size_t off = static_cast<size_t>(sr) * d.cols + sc;
+          float g[V], mo[V], mn[V];
+          Vec16<E>::unpack(graw[q][it], g);
+          Vec16<E>::unpack(mraw[q][it], mo);
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            mn[k] = fmaf(beta, mo[k], g[k]);
+            u[k] = nesterov ? fmaf(beta, mn[k], g[k]) : mn[k];
+            ssq[q] = fmaf(u[k], u[k], ssq[q]);
+          }
+          gst_stream(M + off, Vec16<E>::pack(mn));
+        } else {
+#pragma unroll
+          for (int k = 0; k < V; ++k) u[k] = 0.f;
         }
-        gst_stream(M + off, Vec16<E>::pack(mn));
-      } else {
-#pragma unroll
-        for (int k = 0; k < V; ++k) u[k] = 0.f;
-      }
-      if (d.tall) {   // four 4-byte words at word cv*4 of staged row r
-        const uint4 pk = Vec16<E>::pack(u);
-        uint32_t* row = reinterpret_cast<uint32_t*>(&sU[r][0]) + cv * 4;
-        row[0] = pk.x;
-        row[1] = pk.y;
-        row[2] = pk.z;
-        row[3] = pk.w;
-      } else {  // same layout: straight to X0
-        gst_stream(X0 + static_cast<size_t>(i0 + r) * d.n_pad + j0 + cv * V, Vec16<E>::pack(u));
+        if (d.tall) {   // four 4-byte words at word cv*4 of staged row r
+          const uint4 pk = Vec16<E>::pack(u);
+          uint32_t* row = reinterpret_cast<uint32_t*>(&sU[q][r][0]) + cv * 4;
+          row[0] = pk.x;
+          row[1] = pk.y;
+          row[2] = pk.z;
+          row[3] = pk.w;
+        } else {  // same layout: straight to X0
+          gst_stream(X0 + static_cast<size_t>(i0s[q] + r) * d.n_pad + j0s[q] + cv * V,
+                     Vec16<E>::pack(u));
+        }
       }
     }
   } else {
-    for (int e = tid; e < SR * SC; e += kThreads) {
-      const int r = e / SC, cc = e % SC;
-      const int sr = sr0 + r, sc = sc0 + cc;
-      float u = 0.f;
-      if (sr < d.rows && sc < d.cols) {
-        const size_t off = static_cast<size_t>(sr) * d.cols + sc;
-        const float g = E::load(G + off);
-        const float mn = fmaf(beta, E::load(M + off), g);
-        u = nesterov ? fmaf(beta, mn, g) : mn;
-        ssq = fmaf(u, u, ssq);
-        M[off] = E::from_f32(mn);
+    for (int q = 0; q < nsub; ++q) {
+      const int sr0 = d.tall ? j0s[q] : i0s[q], sc0 = d.tall ? i0s[q] : j0s[q];
+      for (int e = tid; e < SR * SC; e += kThreads) {
+        const int r = e / SC, cc = e % SC;
+        const int sr = sr0 + r, sc = sc0 + cc;
+        float u = 0.f;
+        if (sr < d.rows && sc < d.cols) {
+          const size_t off = static_cast<size_t>(sr) * d.cols + sc;
+          const float g = E::load(G + off);
+          const float mn = fmaf(beta, E::load(M + off), g);
+          u = nesterov ? fmaf(beta, mn, g) : mn;
+          ssq[q] = fmaf(u, u, ssq[q]);
+          M[off] = E::from_f32(mn);
+        }
+        sU[q][r][cc] = E::from_f32(u);
       }
-      sU[r][cc] = E::from_f32(u);
     }
   }
   __syncthreads();
 
   // Store U into X0 (wide layout, rows 16-byte aligned, padding included):
-  // wide row ii of the block is stored row ii (wide) or stored column ii (tall).
+  // wide row ii of a block is stored row ii (wide) or stored column ii (tall).
   // The vector path of a wide matrix has already stored it.
-  if (!d.tall && !d.vec_ok) {
-    constexpr int VPR = SC / V;
-    for (int e = tid; e < SR * VPR; e += kThreads) {
-      const int ii = e / VPR, jv = e % VPR;
-      S w[V];
+  for (int q = 0; q < nsub; ++q) {
+    if (!d.tall && !d.vec_ok) {
+      constexpr int VPR = SC / V;
+      for (int e = tid; e < SR * VPR; e += kThreads) {
+        const int ii = e / VPR, jv = e % VPR;
+        S w[V];
 #pragma unroll
-      for (int k = 0; k < V; ++k) w[k] = sU[ii][jv * V + k];
-      gst_stream(X0 + static_cast<size_t>(i0 + ii) * d.n_pad + j0 + jv * V, pack_raw(w));
-    }
-  } else if (d.tall) {
-    constexpr int VPR = SR / V;
-    for (int e = tid; e < SC * VPR; e += kThreads) {
-      const int ii = e / VPR, jv = e % VPR;
-      S w[V];
+        for (int k = 0; k < V; ++k) w[k] = sU[q][ii][jv * V + k];
+        gst_stream(X0 + static_cast<size_t>(i0s[q] + ii) * d.n_pad + j0s[q] + jv * V,
+                   pack_raw(w));
+      }
+    } else if (d.tall) {
+      constexpr int VPR = SR / V;
+      for (int e = tid; e < SC * VPR; e += kThreads) {
+        const int ii = e / VPR, jv = e % VPR;
+        S w[V];
 #pragma unroll
-      for (int k = 0; k < V; ++k) w[k] = sU[jv * V + k][ii];
-      gst_stream(X0 + static_cast<size_t>(i0 + ii) * d.n_pad + j0 + jv * V, pack_raw(w));
+        for (int k = 0; k < V; ++k) w[k] = sU[q][jv * V + k][ii];
+        gst_stream(X0 + static_cast<size_t>(i0s[q] + ii) * d.n_pad + j0s[q] + jv * V,
+                   pack_raw(w));
+      }
     }
   }
 
-  // Deterministic block reduction of the sum of squares.
-  ssq = warp_sum(ssq);
-  if ((tid & 63) == 0) sRed[tid >> 6] = ssq;
-  __syncthreads();
-  if (tid == 0) {
-    double s = 0.0;
+  // Deterministic block reductions of the sums of squares, one per block.
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) s += static_cast<double>(sRed[w]);
-    partials[d.ew_tile0 + local] = s;
+  for (int q = 0; q < SUB; ++q) {
+    const float v = warp_sum(ssq[q]);
+    if ((tid & 63) == 0) sRed[q][tid >> 6] = v;
+  }
+  __syncthreads();
+  if (tid < nsub) {
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) sum += static_cast<double>(sRed[tid][w]);
+    partials[d.ew_tile0 + first + tid] = sum;
   }
 }
 

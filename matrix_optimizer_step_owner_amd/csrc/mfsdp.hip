@@ -136,6 +136,7 @@ struct Plan {
   std::vector<size_t> off_x0, off_x1, off_a, off_b;
   size_t total = 0;
   int64_t ew_total = 0, gram_total = 0, upd_total = 0;
+  int64_t ew_wg_total = 0;          // momentum workgroups (kEwSub blocks each)
   // Newton-Schulz groups: matrices split into flop-balanced groups whose
   // iterations run on separate streams (see enqueue_muon).  Per group: its
   // matrices and the offsets/counts of its tile tables (in int2 entries from
@@ -221,6 +222,7 @@ mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t d
     mfsdp_status_t st = make_geom(mats[i], i, &p->geom[i], es);
     if (st != MFSDP_OK) return st;
     p->ew_total += p->geom[i].ew_ntiles;
+    p->ew_wg_total += (p->geom[i].ew_ntiles + kEwSub - 1) / kEwSub;
     const int64_t tm = p->geom[i].m_pad / kTile, tn = p->geom[i].n_pad / kTile;
     p->gram_total += tm * (tm + 1) / 2;
     p->upd_total += tm * tn;
@@ -267,8 +269,8 @@ mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t d
   p->off_descs = off;
   off = align_up(off + n * sizeof(MatDesc), kWsAlign);
   p->off_lists = off;
-  // momentum work list: mat[n], begin[n+1]
-  off = align_up(off + (2 * n + 1) * sizeof(int32_t), kWsAlign);
+  // block work list (mat[n], begin[n+1]) and momentum workgroup list (same form)
+  off = align_up(off + (4 * n + 2) * sizeof(int32_t), kWsAlign);
   // per-tile (matrix, tile) tables, per group: symmetric launches, updates,
   // final update over wide matrices, final update over tall matrices
   p->off_tiles = off;
@@ -472,13 +474,17 @@ hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nest
   wl_ew.mat = lists;
   wl_ew.begin = lists + n;
   wl_ew.n_items = static_cast<int32_t>(n);
+  WorkList wl_mom;
+  wl_mom.mat = lists + 2 * n + 1;
+  wl_mom.begin = lists + 3 * n + 1;
+  wl_mom.n_items = static_cast<int32_t>(n);
   const int2* tiles = reinterpret_cast<const int2*>(ws + p.off_tiles);
   float* scales = reinterpret_cast<float*>(ws + p.off_scales);
   double* partials = reinterpret_cast<double*>(ws + p.off_partials);
 
   hipError_t e = launch(MFSDP_KERNEL_MOMENTUM, stream, [&] {
-    momentum_kernel<E><<<dim3(static_cast<unsigned>(p.ew_total)), dim3(kThreads), 0, stream>>>(
-        descs, wl_ew, partials, beta, nesterov);
+    momentum_kernel<E><<<dim3(static_cast<unsigned>(p.ew_wg_total)), dim3(kThreads), 0,
+                         stream>>>(descs, wl_mom, partials, beta, nesterov);
   });
   if (e != hipSuccess) return e;
   e = launch(MFSDP_KERNEL_NORM, stream, [&] {
@@ -878,18 +884,23 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
     d.vec_ok = (g.cols % static_cast<int64_t>(16 / es)) == 0 ? 1 : 0;
     ew_acc += g.ew_ntiles;
   }
-  // momentum tiles in list order: partial sums of a matrix stay contiguous
-  // in the order the finalization reads them.
+  // blocks (and momentum workgroups) in list order: partial sums of a matrix
+  // stay contiguous in the order the finalization reads them.
   {
     int32_t* mat = lists;
     int32_t* begin = mat + n_mats;
-    int64_t acc = 0;
+    int32_t* wmat = lists + 2 * n_mats + 1;
+    int32_t* wbegin = wmat + n_mats;
+    int64_t acc = 0, wacc = 0;
     for (int64_t i = 0; i < n_mats; ++i) {
-      mat[i] = static_cast<int32_t>(i);
+      mat[i] = wmat[i] = static_cast<int32_t>(i);
       begin[i] = static_cast<int32_t>(acc);
+      wbegin[i] = static_cast<int32_t>(wacc);
       acc += p.geom[i].ew_ntiles;
+      wacc += (p.geom[i].ew_ntiles + kEwSub - 1) / kEwSub;
     }
     begin[n_mats] = static_cast<int32_t>(acc);
+    wbegin[n_mats] = static_cast<int32_t>(wacc);
   }
   // per-group tile tables: each launch's tiles by decreasing K (a matrix's
   // tiles together), balanced over the XCDs
