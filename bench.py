@@ -394,7 +394,7 @@ def main():
         with open(tpath) as f:
             tr = json.load(f)
         if (tr.get("kernel") == dominant and tr.get("workload") == args.workload
-                and tr.get("source_sha256") == profiling.kernel_source_hash()):
+                and tr.get("source_sha256") == profiling.kernel_source_hash(dominant)):
             roof["traffic"] = tr.get("bytes_per_launch")
 
     kernels = {}

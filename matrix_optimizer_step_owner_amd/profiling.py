@@ -43,14 +43,22 @@ _NS_MODES = {"0": "gram", "1": "poly", "2": "update", "3": "final_wide", "4": "f
              "5": "syrk"}
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the HIP sources of the library (identifies a kernel build)."""
+#: HIP sources that compile into each kind of kernel (the device code whose
+#: traffic a counter run measures)
+_KERNEL_SOURCES = {"ns": ("common.hpp", "ns_gemm.hpp"),
+                   "elementwise": ("common.hpp", "ew_kernels.hpp")}
+_NS_KINDS = {"gram", "poly", "update", "final", "final_wide", "final_tall", "syrk"}
+
+
+def kernel_source_hash(kind: str = "update") -> str:
+    """sha256 over the HIP sources that define kernel kind ``kind`` (the NS
+    product kernel for gram/poly/update/final/syrk, the elementwise kernels
+    otherwise): it identifies the device code a traffic figure was taken on."""
     d = os.path.join(PKG_DIR, "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".hpp", ".h")):
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in _KERNEL_SOURCES["ns" if kind in _NS_KINDS else "elementwise"]:
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -247,7 +255,7 @@ def main(argv=None) -> None:
                "fetch_calibration_factor": tr["FETCH_SIZE"]["factor"],
                "write_calibration_factor": tr["WRITE_SIZE"]["factor"],
                "dispatches": tr["FETCH_SIZE"]["dispatches"],
-               "source_sha256": kernel_source_hash(),
+               "source_sha256": kernel_source_hash(a.kernel),
                "command": a.command}
         with open(a.out, "w") as f:
             json.dump(doc, f, indent=1)

@@ -57,7 +57,9 @@ def test_stats_summary_and_cli(tmp_path):
                     "--kernel", "update", "--workload", "w", "--command", "c", "--out", str(tj)])
     doc = json.loads(tj.read_text())
     assert doc["bytes_per_launch"] == 15.0 * 1024
-    assert doc["source_sha256"] == profiling.kernel_source_hash()
+    assert doc["source_sha256"] == profiling.kernel_source_hash("update")
+    assert profiling.kernel_source_hash("update") == profiling.kernel_source_hash("gram")
+    assert profiling.kernel_source_hash("update") != profiling.kernel_source_hash("momentum")
 
 
 def test_counter_table_derived_columns(tmp_path):
