@@ -47,11 +47,24 @@ METRIC = "owner-local Muon step ms and Newton-Schulz TFLOP/s (% bf16 MFMA peak)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
-KINDS = ("momentum", "norm", "gram", "poly", "update", "final", "apply", "adamw")
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs x 128 FMA lanes x 2.4 GHz)
+KINDS = ("momentum", "norm", "gram", "poly", "update", "final", "apply", "adamw", "small")
 #: cold-cache pass: bytes overwritten before each timed step (2x the 256 MB
 #: MALL) and the most steps it times
 FLUSH_BYTES = 512 << 20
 COLD_REPS = 20
+
+
+def small_path(m, n):
+    """Whether the library runs a matrix's Newton-Schulz chain whole in one
+    workgroup (the rule of ns_small.hpp: m <= 128, the iterate and both m x m
+    products, rows padded to an odd number of 16-byte chunks, within 38400
+    LDS floats, at most 1024 four-by-four output blocks: two per thread)."""
+    def pitch(c):
+        return 4 * (((c + 3) // 4) | 1)
+    m4 = (m + 3) // 4 * 4
+    return (m <= 128 and m4 * (pitch(n) + 2 * pitch(m)) <= 38400
+            and ((m + 3) // 4) * ((n + 3) // 4) <= 1024)
 
 
 def ns_flops_by_kind(shapes):
@@ -368,14 +381,21 @@ def main():
             per_kind[k] = {"avg_ms": tot / cnt, "launches": cnt,
                            "ms_per_step": tot / args.steps}
 
-    flops = ns_flops_by_kind(shapes)
-    ns_flops_step = wl.ns_steps * sum(flops.values())
-    ns_kernel_ms = sum(per_kind[k]["ms_per_step"] for k in ("gram", "poly", "update", "final")
-                       if k in per_kind)
+    small = [(r, c) for r, c in shapes if small_path(min(r, c), max(r, c))]
+    flops = ns_flops_by_kind([s for s in shapes if s not in small])
+    # one launch of the small-matrix kernel runs every iteration
+    flops["small"] = wl.ns_steps * sum(ns_flops_by_kind(small).values())
+    ns_flops_step = wl.ns_steps * sum(ns_flops_by_kind(shapes).values())
+    ns_kernel_ms = sum(per_kind[k]["ms_per_step"]
+                       for k in ("gram", "poly", "update", "final", "small") if k in per_kind)
     peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_FP32_MFMA_TFLOPS
     dominant = max(per_kind, key=lambda k: per_kind[k]["ms_per_step"])
     ew = elementwise_bytes(shapes, es, wl.tail_n)
-    if dominant in flops:
+    if dominant == "small":   # fp32 dot products on the vector ALUs, either dtype
+        achieved = flops["small"] / (per_kind["small"]["avg_ms"] * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS}
+    elif dominant in flops:
         achieved = flops[dominant] / (per_kind[dominant]["avg_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak}

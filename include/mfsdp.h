@@ -349,7 +349,8 @@ typedef enum mfsdp_kernel_kind {
   MFSDP_KERNEL_FINAL = 7,     /* last update, applies W (2 launches) */
   MFSDP_KERNEL_STATS_PREP = 8,/* gradient copies for the statistics   */
   MFSDP_KERNEL_SYRK = 9,      /* L, R statistics products            */
-  MFSDP_KERNEL_KINDS = 10
+  MFSDP_KERNEL_SMALL = 10,    /* whole NS chain + apply of small matrices */
+  MFSDP_KERNEL_KINDS = 11
 } mfsdp_kernel_kind_t;
 
 mfsdp_status_t mfsdp_timing_enable(int enable);

@@ -19,7 +19,8 @@ NS_EPS = 1e-7
 #: size of the static device scratch of mfsdp_muon_step_noalloc (bytes)
 NOALLOC_SCRATCH_BYTES = 256 << 20
 KERNEL_KINDS = {"momentum": 0, "norm": 1, "gram": 2, "poly": 3, "update": 4,
-                "apply": 5, "adamw": 6, "final": 7, "stats_prep": 8, "syrk": 9}
+                "apply": 5, "adamw": 6, "final": 7, "stats_prep": 8, "syrk": 9,
+                "small": 10}
 
 #: Every symbol include/mfsdp.h declares.
 EXPORTED = ("mfsdp_muon_workspace_size", "mfsdp_muon_step", "mfsdp_muon_step_noalloc",

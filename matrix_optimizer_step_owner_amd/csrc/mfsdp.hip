@@ -27,6 +27,7 @@
 #include "common.hpp"
 #include "ew_kernels.hpp"
 #include "ns_gemm.hpp"
+#include "ns_small.hpp"
 #include "planner.hpp"
 #include "stats_kernels.hpp"
 #include "tail_kernels.hpp"
@@ -126,12 +127,15 @@ hipError_t launch(int kind, hipStream_t stream, F&& f) {
 struct MatGeom {
   int64_t rows, cols, m, n, m_pad, n_pad;
   bool tall;
+  bool small;   // whole Newton-Schulz chain in one workgroup (ns_small.hpp)
   int64_t ew_tiles_j, ew_ntiles, ew_th, ew_tw;
 };
 
 struct Plan {
   std::vector<MatGeom> geom;
   size_t off_descs = 0, off_lists = 0, off_tiles = 0, off_scales = 0, off_partials = 0;
+  size_t off_small = 0;             // int32 indices of the small matrices
+  std::vector<int64_t> small;
   size_t blob_bytes = 0;            // descriptors + work lists (host upload)
   std::vector<size_t> off_x0, off_x1, off_a, off_b;
   size_t total = 0;
@@ -199,6 +203,7 @@ mfsdp_status_t make_geom(const mfsdp_matrix_t& mt, int64_t idx, MatGeom* g, size
   g->n = std::max(mt.rows, mt.cols);
   g->m_pad = round_up(g->m, kTile);
   g->n_pad = round_up(g->n, kTile);
+  g->small = small_path(g->m, g->n);
   // Kernels address an iterate with 32-bit byte offsets from its base.
   if (g->n_pad > (int64_t(1) << 24) || g->m_pad * g->n_pad >= (int64_t(1) << 31) ||
       g->m_pad * g->n_pad * static_cast<int64_t>(es) >= (int64_t(1) << 32))
@@ -223,22 +228,31 @@ mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t d
     if (st != MFSDP_OK) return st;
     p->ew_total += p->geom[i].ew_ntiles;
     p->ew_wg_total += (p->geom[i].ew_ntiles + kEwSub - 1) / kEwSub;
+    if (p->geom[i].small) {
+      p->small.push_back(i);
+      continue;
+    }
     const int64_t tm = p->geom[i].m_pad / kTile, tn = p->geom[i].n_pad / kTile;
     p->gram_total += tm * (tm + 1) / 2;
     p->upd_total += tm * tn;
   }
-  // flop-balanced groups (largest first onto the least loaded group)
+  // flop-balanced groups of the tiled matrices (largest first onto the least
+  // loaded group); small matrices are outside the groups
   {
-    const int ng = choose_groups(n, p->upd_total, max_groups);
-    p->groups.assign(ng, Plan::Group{});
-    std::vector<int64_t> order(n), work(n);
-    std::vector<int64_t> load(ng, 0);
+    std::vector<int64_t> order, work(n, 0);
     for (int64_t i = 0; i < n; ++i) {
       const MatGeom& g = p->geom[i];
+      if (g.small) continue;
       const int64_t tm = g.m_pad / kTile, tn = g.n_pad / kTile;
       work[i] = tm * (tm + 1) / 2 * (g.n_pad + g.m_pad) + tm * tn * g.m_pad;
-      order[i] = i;
+      order.push_back(i);
     }
+    const int ng = order.empty()
+                       ? 0
+                       : choose_groups(static_cast<int64_t>(order.size()), p->upd_total,
+                                       max_groups);
+    p->groups.assign(ng, Plan::Group{});
+    std::vector<int64_t> load(ng, 0);
     std::stable_sort(order.begin(), order.end(),
                      [&](int64_t a, int64_t b) { return work[a] > work[b]; });
     for (int64_t i : order) {
@@ -275,6 +289,8 @@ mfsdp_status_t build_plan(const mfsdp_matrix_t* mats, int64_t n, mfsdp_dtype_t d
   // final update over wide matrices, final update over tall matrices
   p->off_tiles = off;
   off = align_up(off + (p->gram_total + 2 * p->upd_total) * sizeof(int2), kWsAlign);
+  p->off_small = off;
+  off = align_up(off + p->small.size() * sizeof(int32_t), kWsAlign);
   p->blob_bytes = off;
   p->off_scales = off;
   off = align_up(off + n * sizeof(float), kWsAlign);
@@ -500,7 +516,23 @@ hipError_t enqueue_muon(const Plan& p, int64_t n, char* ws, float beta, int nest
     });
   }
 
+  if (!p.small.empty()) {
+    SmallNsArgs sa;
+    sa.mats = reinterpret_cast<const int32_t*>(ws + p.off_small);
+    sa.a = a;
+    sa.b = b;
+    sa.c = c;
+    sa.ns_steps = ns_steps;
+    sa.decay = decay;
+    e = launch(MFSDP_KERNEL_SMALL, stream, [&] {
+      small_ns_kernel<E><<<dim3(static_cast<unsigned>(p.small.size())), dim3(kSmallThreads), 0,
+                           stream>>>(descs, scales, sa);
+    });
+    if (e != hipSuccess) return e;
+  }
+
   const int ng = static_cast<int>(p.groups.size());
+  if (ng == 0) return hipSuccess;
   if (ng == 1)
     return enqueue_ns_group<E>(p, p.groups[0], descs, tiles, scales, decay, ns_steps, a, b, c,
                                stream);
@@ -931,6 +963,11 @@ static mfsdp_status_t muon_step_impl(const mfsdp_matrix_t* mats, int64_t n_mats,
   st = refuse_capture(stream);
   if (st != MFSDP_OK) return st;
   if (log_enabled()) log_plan(p, n_mats, dtype, ns_steps, stream);
+
+  {
+    int32_t* sm = reinterpret_cast<int32_t*>(blob.data() + p.off_small);
+    for (size_t j = 0; j < p.small.size(); ++j) sm[j] = static_cast<int32_t>(p.small[j]);
+  }
 
   hipError_t e = hipMemcpyAsync(ws, blob.data(), p.blob_bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "descriptor upload: %s", hipGetErrorString(e));

@@ -67,7 +67,8 @@ def short_name(kernel: str) -> str:
     m = re.search(r"ns_gemm_kernel<mfsdp::Elem(BF16|F32), (\d)>", kernel)
     if m:
         return _NS_MODES[m.group(2)] + ("" if m.group(1) == "BF16" else "_f32")
-    for key, name in (("momentum_kernel", "momentum"), ("norm_finalize_kernel", "norm"),
+    for key, name in (("small_ns_kernel", "small"), ("momentum_kernel", "momentum"),
+                      ("norm_finalize_kernel", "norm"),
                       ("adamw_kernel", "adamw"), ("apply_x0_kernel", "apply")):
         if key in kernel:
             return name

@@ -65,6 +65,18 @@ def test_ns_kernels_use_no_scratch(device_build):
         assert v.get("VGPRs Spill", 0) == 0, (k, v)
 
 
+def test_small_matrix_kernel_uses_no_scratch(device_build):
+    # the whole-chain kernel of small matrices keeps its output blocks in
+    # registers (both dtypes) and its LDS within the 160 KB of a CU
+    _, remarks = device_build
+    usage = kernel_usage(remarks)
+    small = {k: v for k, v in usage.items() if "small_ns_kernel" in k}
+    assert len(small) == 2, list(usage)
+    for k, v in small.items():
+        assert v.get("ScratchSize", 0) == 0, (k, v)
+        assert v.get("LDS Size", 0) <= 160 * 1024, (k, v)
+
+
 def test_steady_state_ns_kernels_fit_the_instruction_cache(device_build):
     obj, _ = device_build
     bundler = os.path.join(LLVM, "clang-offload-bundler")

@@ -396,3 +396,38 @@ def test_launch_plan_log(monkeypatch, capfd):
     err = capfd.readouterr().err
     assert "mfsdp_muon_step: 5 matrices, bf16, ns_steps 5" in err, err
     assert "group 0 on the caller's stream" in err and "2048x2048*1" in err, err
+
+
+SMALL_MIX = [(64, 128), (128, 64), (96, 96), (1, 5), (7, 300), (100, 100), (100, 200),
+             (130, 130), (512, 256)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_small_matrices_mixed_with_tiled_ones(dtype):
+    # Matrices with m <= 128 whose iterate and products fit in LDS run their
+    # whole Newton-Schulz chain in one workgroup; the others (100 x 200,
+    # 130 x 130, 512 x 256 here) take the tiled MFMA path.  Every matrix against the
+    # oracle, and the path depends on the shape alone: each matrix stepped
+    # alone gives bitwise the result it gets in the mixed call.
+    Ws, Gs, Ms = wlm.random_matrix_inputs(SMALL_MIX, dtype, seed=31)
+    hp = muon_hparams()
+    st, _ = run_and_check(Ws, Gs, Ms, hp, dtype, label=f"small mix {dtype}")
+    for i in range(len(SMALL_MIX)):
+        one = GpuStep([Ws[i]], [Gs[i]], [Ms[i]])
+        one.run(**hp)
+        assert torch.equal(one.W[0], st.W[i]) and torch.equal(one.U[0], st.U[i]), i
+
+
+@pytest.mark.parametrize("variant", ["ns1", "cubic", "no_nesterov"])
+def test_small_matrix_variants(variant):
+    shapes = [(64, 128), (96, 96), (33, 17)]
+    Ws, Gs, Ms = wlm.random_matrix_inputs(shapes, torch.float32, seed=32)
+    hp = muon_hparams()
+    if variant == "ns1":
+        hp["ns_steps"] = 1
+    elif variant == "cubic":
+        hp["abc"] = (1.5, -0.5, 0.0)
+        hp["ns_steps"] = 12
+    else:
+        hp["nesterov"] = False
+    run_and_check(Ws, Gs, Ms, hp, torch.float32, label=f"small {variant}")
