@@ -289,7 +289,7 @@ def test_prepared_step_object_equals_function():
         assert torch.equal(a.W[i], b.W[i]) and torch.equal(a.M[i], b.M[i]), i
 
 
-@pytest.mark.parametrize("groups", ["1", "2"])
+@pytest.mark.parametrize("groups", ["1", "2", "small"])
 def test_nan_gradient_stays_in_its_matrix(monkeypatch, groups):
     # Non-finite inputs propagate and nothing checks them, but matrices are
     # independent: a NaN in one matrix's gradient must leave every other
@@ -297,12 +297,18 @@ def test_nan_gradient_stays_in_its_matrix(monkeypatch, groups):
     # stream and with two Newton-Schulz stream groups.  In the poisoned
     # matrix, M' differs from the clean M' only at the NaN element, and its
     # norm (hence every NS iterate, O and W') is NaN.
-    monkeypatch.setenv("MFSDP_NS_GROUPS", groups)
-    Ws, Gs, Ms = _subset_inputs()
+    # "small": small-matrix kernels (one workgroup each) beside a tiled one
+    if groups == "small":
+        Ws, Gs, Ms = wlm.random_matrix_inputs([(64, 128), (120, 96), (512, 256), (33, 17)],
+                                              torch.bfloat16, seed=5)
+        k, (r, c) = 1, (70, 33)
+    else:
+        monkeypatch.setenv("MFSDP_NS_GROUPS", groups)
+        Ws, Gs, Ms = _subset_inputs()
+        k, (r, c) = 1, (700, 33)
     hp = muon_hparams()
     clean = GpuStep(Ws, Gs, Ms)
     clean.run(**hp)
-    k, (r, c) = 1, (700, 33)
     Gbad = [g.clone() for g in Gs]
     Gbad[k][r, c] = float("nan")
     bad = GpuStep(Ws, Gbad, Ms)

@@ -62,7 +62,9 @@ def run_trajectory(shapes, dtype, steps, seed):
 
 
 def test_fp32_trajectory_50_steps():
-    shapes = [(64, 128), (128, 64), (96, 96)]
+    # the tiny workload's shapes (the small-matrix kernel) and two that take
+    # the tiled MFMA path (m = 200 and 130 exceed the small kernel's bound)
+    shapes = [(64, 128), (128, 64), (96, 96), (300, 200), (130, 130)]
     T = 50
     W0, gpu, ref = run_trajectory(shapes, torch.float32, T, seed=100)
     worst = 0.0
@@ -77,8 +79,9 @@ def test_fp32_trajectory_50_steps():
 
 
 def test_bf16_trajectory_10_steps():
-    # a tall, a wide and a square matrix; 384 is a tile and a half (ragged)
-    shapes = [(512, 256), (256, 768), (384, 384)]
+    # a tall, a wide and a square matrix; 384 is a tile and a half (ragged);
+    # 120 x 96 takes the small-matrix kernel
+    shapes = [(512, 256), (256, 768), (384, 384), (120, 96)]
     T = 10
     W0, gpu, ref = run_trajectory(shapes, torch.bfloat16, T, seed=200)
     for t in range(T):
