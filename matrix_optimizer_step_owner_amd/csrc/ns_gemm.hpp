@@ -9,10 +9,11 @@
 // first gram uses the un-normalized U with alpha = s^2 and the first update
 // alpha = s, where s = 1 / (||U||_F + eps).
 //
-// Kernel shape: 256 threads (4 waves) per 256x256 output tile, each wave a
-// 128x128 quadrant of 4x4 MFMA 32x32 blocks.  Operand panels (one K step: 64
+// Kernel shape: one workgroup per 256x256 output tile, of 4 waves (each a
+// 128x128 quadrant of 4x4 MFMA 32x32 blocks; the Gram products) or 8 waves
+// (each 128x64, 4x2 blocks; the other products).  Operand panels (one K step: 64
 // bf16 or 32 fp32 per row) go from global memory straight into LDS
-// (global_load_lds_dwordx4, no register staging), double buffered (128 KB);
+// (global_load_lds_dwordx4, no register staging) in four 32 KB stages;
 // rows are XOR-swizzled in 16-byte chunks so fragment reads are free of bank
 // conflicts.  The update's K-strided operand X keeps its row-major layout in
 // LDS and is read with the gfx950 transposing LDS load (ds_read_b64_tr_b16),
@@ -245,26 +246,50 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // chunk, which (row >> 2) & 3 spreads over all 16 bank groups.
 __device__ __forceinline__ int kswz(int row) { return (row >> 2) & 3; }
 
-// Which DMA piece (0..7, or -1 for none) a K step issues in MFMA slot idx of
-// sub-step sub: the eight 1 KB pieces of a stage are spread over the step,
-// one every fourth MFMA slot of both sub-steps, so that the vector-memory
-// queue never holds up the MFMA issue for long.  The four waves of a CU share
-// one texture addresser: issuing a step's pieces in a burst (the first eight
-// slots of sub-step 0) kept it busy long enough to stall MFMA issue and was 3%
-// slower on the d=2048 block.
-__host__ __device__ constexpr int dma_slot_piece(int sub, int idx) {
-  return (idx & 3) == 0 ? 4 * sub + idx / 4 : -1;
+// Waves per 256x256 tile: 4 (one per SIMD, each wave a 128 x 128 quadrant,
+// 256 accumulator registers) or 8 (two per SIMD, each wave 128 x 64, 128
+// accumulator registers).  With two waves per SIMD, one wave's epilogue
+// loads, LDS staging and stores overlap the other's: the polynomial, update
+// and apply launches run 1-11% faster with 8 waves.  The Gram products (and
+// the statistics product) keep 4: their K loops are the longest and the NT
+// fragment reads of 128 x 64 wave tiles (six per eight MFMAs instead of eight
+// per sixteen) made them 3-6% slower.
+__host__ __device__ constexpr int ns_waves(int mode) {
+  return (mode == kModeGram || mode == kModeSyrk) ? 4 : 8;
 }
-// DMAs that may stay in flight at the barrier of step t: the eight of step
-// t - 1 and the four that step t issued before its barrier (step t + 1's must
-// be done).
-#define MFSDP_VM_IN_FLIGHT "12"
+__host__ __device__ constexpr int ns_threads(int mode) { return 64 * ns_waves(mode); }
+
+template <int W>
+struct NsShape {
+  static_assert(W == 4 || W == 8, "4 or 8 waves per tile");
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kWaveCols = 2 * kTile / W;       // output columns per wave
+  static constexpr int kWaveColsLog2 = W == 8 ? 6 : 7;
+  static constexpr int kWaveRowLog2 = W == 8 ? 2 : 1;   // wave index -> 128-row half
+  static_assert(kWaveCols == 1 << kWaveColsLog2 && W / 2 == 1 << kWaveRowLog2, "powers of two");
+  static constexpr int kBJ = kWaveCols / 32;            // 32-column MFMA blocks per wave
+  static constexpr int kSlots = 4 * kBJ;                // MFMAs per wave per K sub-step
+  static constexpr int kPieces = 32 / W;                // 1 KB DMA pieces per wave per K step
+  static constexpr int kPPW = kPieces / 2;              // of them per operand panel
+  static constexpr int kEpIt = 64 * kTile / 8 / kThreads;   // epilogue 8-element groups per thread
+};
+
+// Which DMA piece (0..2*bj-1, or -1 for none) a K step issues in MFMA slot
+// idx of sub-step sub, for waves with bj 32-column blocks: the pieces of a
+// stage are spread over the step, one every fourth MFMA slot of both
+// sub-steps, so that the vector-memory queue never holds up the MFMA issue
+// for long.  The waves of a CU share one texture addresser: issuing a step's
+// pieces in a burst (the first eight slots of sub-step 0) kept it busy long
+// enough to stall MFMA issue and was 3% slower on the d=2048 block.
+__host__ __device__ constexpr int dma_slot_piece(int bj, int sub, int idx) {
+  return (idx & 3) == 0 ? bj * sub + idx / 4 : -1;
+}
 
 // Tile rows per band of the update's tile order (see ns_gemm_kernel).
 constexpr int kUpdBandRows = 4;
 
 template <class E, int MODE>
-__global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
+__global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
     const MatDesc* __restrict__ descs, const int2* __restrict__ tiles,
     const float* __restrict__ scales, NsEpi ep) {
   using S = typename E::storage_t;
@@ -272,6 +297,13 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   constexpr int BK = 4 * V;             // K elements per 64-byte panel row
   constexpr int PANEL = kTile * 4;      // uint4 per operand panel (16 KB)
   constexpr int kStages = 4;            // LDS pipeline depth (4 x 32 KB)
+  using SH = NsShape<ns_waves(MODE)>;
+  constexpr int kNsWaves = ns_waves(MODE);
+  constexpr int kNsThreads = SH::kThreads;
+  constexpr int kWaveCols = SH::kWaveCols, kWaveColsLog2 = SH::kWaveColsLog2;
+  constexpr int kWaveRowLog2 = SH::kWaveRowLog2;
+  constexpr int kBJ = SH::kBJ, kSlots = SH::kSlots;
+  constexpr int kPieces = SH::kPieces, kPPW = SH::kPPW, kEpIt = SH::kEpIt;
 
   // Pipeline stages, each holding the P panel then the Q panel.  Separate
   // objects so that the compiler can tell a DMA into one stage from reads of
@@ -328,20 +360,21 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   // at k*32 + (c ^ 4*(k & 3)); fp32: 16 k-rows x 64 chunks, unswizzled.
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave >> kWaveRowLog2, wc = wave & (kNsWaves / 2 - 1);
   const int lrow = lane & 31, lhalf = lane >> 5;
 
-  // DMA piece q (0..7) of one K step: pieces 0..3 fill the P panel, 4..7 the
-  // Q panel; each piece is one 1 KB wave instruction.  The per-lane byte
-  // offset of a piece is fixed for the whole K loop; only the uniform base
-  // moves with k0 (SGPR base + constant VGPR offset, no address VALU).
-  uint32_t doff[8];
+  // DMA piece q (0..kPieces-1) of one K step, per wave: the first kPPW fill
+  // this wave's share of the P panel, the others its share of the Q panel;
+  // each piece is one 1 KB wave instruction.  The per-lane byte offset of a
+  // piece is fixed for the whole K loop; only the uniform base moves with k0
+  // (SGPR base + constant VGPR offset, no address VALU).
+  uint32_t doff[kPieces];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int u = wave * 256 + (q & 3) * 64 + lane;
-    if (q < 4 || !kUpd) {
-      const int ld = q < 4 ? ldp : ldq;
-      const int r0 = q < 4 ? row0 : col0;
+  for (int q = 0; q < kPieces; ++q) {
+    const int u = wave * (kPPW * 64) + (q % kPPW) * 64 + lane;
+    if (q < kPPW || !kUpd) {
+      const int ld = q < kPPW ? ldp : ldq;
+      const int r0 = q < kPPW ? row0 : col0;
       const int row = u >> 2, c = (u & 3) ^ kswz(row);
       doff[q] = static_cast<uint32_t>((static_cast<size_t>(r0 + row) * ld + c * V) * sizeof(S));
     } else {
@@ -353,19 +386,19 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   }
   // Every DMA destination is a link-time constant (the stage object and the
   // piece) plus this wave's uniform offset: no per-lane address work.
-  const uint32_t wave_off = static_cast<uint32_t>(wave) * 4096u;
+  const uint32_t wave_off = static_cast<uint32_t>(wave) * (kPPW * 1024u);
   auto dma_piece = [&](auto stage_c, int k0, int q) {
     constexpr int stage = decltype(stage_c)::value;
     const uint4* sbuf = stage == 0 ? st0 : stage == 1 ? st1 : stage == 2 ? st2 : st3;
     const char* base;
-    if (q < 4)
+    if (q < kPPW)
       base = reinterpret_cast<const char*>(P + k0);
     else if (!kUpd)
       base = reinterpret_cast<const char*>(Q + k0);
     else
       base = reinterpret_cast<const char*>(Q + static_cast<size_t>(k0) * ldq);
-    const uint32_t dst = lds_addr(sbuf) + wave_off + (q < 4 ? 0u : PANEL * 16u) +
-                         static_cast<uint32_t>(q & 3) * 1024u;
+    const uint32_t dst = lds_addr(sbuf) + wave_off + (q < kPPW ? 0u : PANEL * 16u) +
+                         static_cast<uint32_t>(q % kPPW) * 1024u;
     lds_dma16(dst, doff[q], base);
   };
 
@@ -374,8 +407,9 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   // (bf16: K = 8*(2s + l/32) .. +8) of output row l%32 of each 32-row block.
   // Read piece p: 0..3 the P fragments fa[i]; then the Q fragments (NT: one
   // piece per fb[j]; bf16 update: two transposing reads per fb[j]).
-  constexpr int kReadPieces = (kUpd && V == 8) ? 12 : 8;
-  auto read_piece = [&](const uint4* buf, int s, int p, uint4 (&fa)[4], uint4 (&fb)[4]) {
+  constexpr int kReadPieces = (kUpd && V == 8) ? 4 + 2 * kBJ : 4 + kBJ;
+  static_assert(kReadPieces <= kSlots, "one fragment read per MFMA slot at most");
+  auto read_piece = [&](const uint4* buf, int s, int p, uint4 (&fa)[4], uint4 (&fb)[kBJ]) {
     const int c = 2 * s + lhalf;
     if (p < 4) {
       const int row = wr * 128 + p * 32 + lrow;
@@ -385,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     const uint4* qp = buf + PANEL;
     if constexpr (!kUpd) {
       const int j = p - 4;
-      const int row = wc * 128 + j * 32 + lrow;
+      const int row = wc * kWaveCols + j * 32 + lrow;
       fb[j] = qp[row * 4 + (c ^ kswz(row))];
     } else if constexpr (V == 8) {
       // Transposing read: within each 16-lane group, lane i points at k-row
@@ -393,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
       // at k-rows kb .. kb+3.
       const int j = (p - 4) >> 1, r = (p - 4) & 1;
       const int il = lane & 15;
-      const int n = wc * 128 + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (il & 3);
+      const int n = wc * kWaveCols + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (il & 3);
       const int kk = 16 * s + 8 * lhalf + 4 * r + (il >> 2);
       const int byte = kk * 512 + (((n >> 3) ^ (4 * (kk & 3))) << 4) + ((n & 7) << 1);
       const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -412,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     } else {
       const int j = p - 4;
       const float* qf = reinterpret_cast<const float*>(qp);
-      const int n = wc * 128 + j * 32 + lrow;
+      const int n = wc * kWaveCols + j * 32 + lrow;
       const int kk = 4 * c;
       fb[j] = make_uint4(__float_as_uint(qf[(kk + 0) * kTile + n]),
                          __float_as_uint(qf[(kk + 1) * kTile + n]),
@@ -421,15 +455,15 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     }
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][kBJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < kBJ; ++j) acc[i][j] = f32x16_t{};
 
-  uint4 fa[2][4], fb[2][4];
+  uint4 fa[2][4], fb[2][kBJ];
 
-  // One K step t on stage buffer X.  Sub-step 0 issues its 16 MFMAs one per
+  // One K step t on stage buffer X.  Sub-step 0 issues its kSlots MFMAs one per
   // slot; each slot also issues one fragment read of sub-step 1 and (when
   // DMA) one DMA piece of step t + kStages - 1 into stage Y, the buffer of
   // step t - 1.  Then: wait until the DMA of step t + 1 has landed (the two
@@ -443,29 +477,35 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     constexpr bool has_next = decltype(next_c)::value;
     constexpr bool wait_all = decltype(wait_all_c)::value;
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      Mma<E>::run(acc[idx >> 2][idx & 3], fa[0][idx >> 2], fb[0][idx & 3]);
+    for (int idx = 0; idx < kSlots; ++idx) {
+      Mma<E>::run(acc[idx / kBJ][idx % kBJ], fa[0][idx / kBJ], fb[0][idx % kBJ]);
       if (idx < kReadPieces) read_piece(X, 1, idx, fa[1], fb[1]);
       if constexpr (do_dma) {
-        if (dma_slot_piece(0, idx) >= 0) dma_piece(Y, k_dma, dma_slot_piece(0, idx));
+        if (dma_slot_piece(kBJ, 0, idx) >= 0) dma_piece(Y, k_dma, dma_slot_piece(kBJ, 0, idx));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     // Block barrier without the release fence of __syncthreads(), which would
     // also wait for the DMAs still in flight; the memory clobber keeps the
     // compiler from moving LDS accesses across it.
+    // DMAs that may stay in flight at the barrier of step t: the kPieces of
+    // step t - 1 and the half that step t issued before its barrier (step
+    // t + 1's must be done).
+    static_assert(kPieces == 8 || kPieces == 4, "wait counts below");
     if constexpr (wait_all)
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (kPieces == 8)
+      asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
-      asm volatile("s_waitcnt vmcnt(" MFSDP_VM_IN_FLIGHT ") lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      Mma<E>::run(acc[idx >> 2][idx & 3], fa[1][idx >> 2], fb[1][idx & 3]);
+    for (int idx = 0; idx < kSlots; ++idx) {
+      Mma<E>::run(acc[idx / kBJ][idx % kBJ], fa[1][idx / kBJ], fb[1][idx % kBJ]);
       if constexpr (has_next) {
         if (idx < kReadPieces) read_piece(N, 0, idx, fa[0], fb[0]);
       }
       if constexpr (do_dma) {
-        if (dma_slot_piece(1, idx) >= 0) dma_piece(Y, k_dma, dma_slot_piece(1, idx));
+        if (dma_slot_piece(kBJ, 1, idx) >= 0) dma_piece(Y, k_dma, dma_slot_piece(kBJ, 1, idx));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -481,12 +521,16 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   const int nk = K / BK;                // multiple of 8: K is a multiple of 256
   // prologue: steps 0..2 in flight, wait for step 0
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dma_piece(S0{}, 0, q);
+  for (int q = 0; q < kPieces; ++q) dma_piece(S0{}, 0, q);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dma_piece(S1{}, BK, q);
+  for (int q = 0; q < kPieces; ++q) dma_piece(S1{}, BK, q);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dma_piece(S2{}, 2 * BK, q);
-  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  for (int q = 0; q < kPieces; ++q) dma_piece(S2{}, 2 * BK, q);
+  // the two later stages may stay in flight
+  if constexpr (kPieces == 8)
+    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int p = 0; p < kReadPieces; ++p) read_piece(st0, 0, p, fa[0], fb[0]);
   int t = 0;
@@ -505,19 +549,23 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
 
   // ---- epilogue through LDS -------------------------------------------------
   // acc[i][j][r] sits at tile row wr*128 + i*32 + (r/4)*8 + lhalf*4 + r%4,
-  // tile column wc*128 + j*32 + lrow.  For each i, the four waves stage their
-  // 32 x 128 slices in LDS (fp32), then all threads process the 64 x 256 block
-  // with 16-byte row-contiguous global accesses (pass A); a second,
+  // tile column wc*kWaveCols + j*32 + lrow.  For each i, the waves stage their
+  // 32 x kWaveCols slices in LDS (fp32), then all threads process the 64 x 256
+  // block with 16-byte row-contiguous global accesses (pass A); a second,
   // column-wise pass writes the mirrored tile of a symmetric product or the
   // transposed apply of a tall matrix (pass B).  Every global input of a pass
   // is loaded before its first store: the stores may alias the inputs as far
   // as the compiler knows, so interleaving them would serialize on latency.
-  constexpr int SP = 128;               // staged row pitch in floats
+  constexpr int SP = kWaveCols;         // staged row pitch in floats
   // column c of staged row r lives at r*SP + (c ^ 4*((r >> 2) & 7))
   auto sidx = [](int r, int c) { return r * SP + (c ^ (((r >> 2) & 7) << 2)); };
-  // wave slice w lives in stage array w (16 KB of its 32 KB)
+  // wave slice w (32 x kWaveCols floats: 16 or 8 KB) lives in stage array
+  // w / kPer, at slice w % kPer of its 32 KB
+  constexpr int kPer = kNsWaves / 4;
   auto slice_of = [&](int w) -> float* {
-    return reinterpret_cast<float*>(w == 0 ? st0 : w == 1 ? st1 : w == 2 ? st2 : st3);
+    const int sa = w / kPer;
+    float* b = reinterpret_cast<float*>(sa == 0 ? st0 : sa == 1 ? st1 : sa == 2 ? st2 : st3);
+    return b + (w % kPer) * (32 * kWaveCols);
   };
   const float s_norm = scales[k];
   constexpr bool sym = !kUpd;
@@ -535,14 +583,14 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
 
   // pass A coordinates of iteration p: tile row, tile column, staged slice
   auto coordA = [&](int i, int p, int& grow, int& gcol, int& sl, int& r_in, int& c_in) {
-    const int it = p * kThreads + tid;
-    const int rr = it >> 5, cv = it & 31;
-    const int wrr = rr >> 5, wcc = cv >> 4;
+    const int it = p * kNsThreads + tid;
+    const int rr = it >> 5, col = (it & 31) * 8;
+    const int wrr = rr >> 5, wcc = col >> kWaveColsLog2;
     r_in = rr & 31;
-    c_in = (cv & 15) * 8;
-    sl = wrr * 2 + wcc;
+    c_in = col & (kWaveCols - 1);
+    sl = (wrr << kWaveRowLog2) + wcc;
     grow = row0 + wrr * 128 + i * 32 + r_in;
-    gcol = col0 + wcc * 128 + c_in;
+    gcol = col0 + col;
   };
 
   // One 64 x 256 block per accumulator row i; i is a compile-time constant
@@ -550,12 +598,12 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
   // pass B coordinates of iteration p: eight consecutive tile rows of one
   // tile column
   auto coordB = [&](int i, int p, int& gcol, int& grow0, int& sl, int& sub, int& c_in) {
-    const int it = p * kThreads + tid;
+    const int it = p * kNsThreads + tid;
     const int tc = it >> 3, q = it & 7;
-    const int wrr = q >> 2, wcc = tc >> 7;
+    const int wrr = q >> 2, wcc = tc >> kWaveColsLog2;
     sub = q & 3;
-    c_in = tc & 127;
-    sl = wrr * 2 + wcc;
+    c_in = tc & (kWaveCols - 1);
+    sl = (wrr << kWaveRowLog2) + wcc;
     grow0 = row0 + wrr * 128 + i * 32 + sub * 8;
     gcol = col0 + tc;
   };
@@ -565,9 +613,9 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     // global inputs of both passes, issued before the staging so that their
     // latency overlaps it (the weights: pass A for a wide apply, pass B for
     // a tall one)
-    Raw8 xin[8], win[8];
+    Raw8 xin[kEpIt], win[kEpIt];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < kEpIt; ++p) {
       int grow, gcol, sl, r_in, c_in;
       coordA(i, p, grow, gcol, sl, r_in, c_in);
       if (MODE != kModeGram && MODE != kModeSyrk && !(kUpd && ep.fold))
@@ -584,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     {
       float* reg = slice_of(wave);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kBJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           reg[sidx((r >> 2) * 8 + lhalf * 4 + (r & 3), j * 32 + lrow)] = acc[i][j][r];
@@ -593,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
 
     // Pass A: row-major, eight consecutive columns per thread.
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < kEpIt; ++p) {
       int grow, gcol, sl, r_in, c_in;
       coordA(i, p, grow, gcol, sl, r_in, c_in);
       float* slice = slice_of(sl);
@@ -646,7 +694,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(
     if (mirror || tall_apply) {
       __syncthreads();
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
+      for (int p = 0; p < kEpIt; ++p) {
         int gcol, grow0, sl, sub, c_in;
         coordB(i, p, gcol, grow0, sl, sub, c_in);
         const float* slice = slice_of(sl);
