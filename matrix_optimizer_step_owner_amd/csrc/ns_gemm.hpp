@@ -358,6 +358,13 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
   // chunk c of row r stored at r*4 + (c ^ kswz(r)).  The K-strided panel of
   // the update (X, bf16): 32 k-rows x 32 chunks (256 columns), chunk c of row k
   // at k*32 + (c ^ 4*(k & 3)); fp32: 16 k-rows x 64 chunks, unswizzled.
+  // In bf16 the update's P panel is K-strided too: B' (or A) is symmetric, so
+  // its row panel B'[row0..+256, k0..+32] equals the column panel
+  // B'[k0..+32, row0..+256], 32 rows of 512 contiguous bytes.  Each DMA
+  // request then covers whole 128-byte lines instead of 64-byte halves, which
+  // halves the L1-to-L2 requests of that panel: the texture path that feeds
+  // these DMAs is the busiest unit of the K loop on long-K products.
+  constexpr bool kPT = kUpd && V == 8;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> kWaveRowLog2, wc = wave & (kNsWaves / 2 - 1);
@@ -372,16 +379,16 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
 #pragma unroll
   for (int q = 0; q < kPieces; ++q) {
     const int u = wave * (kPPW * 64) + (q % kPPW) * 64 + lane;
-    if (q < kPPW || !kUpd) {
-      const int ld = q < kPPW ? ldp : ldq;
-      const int r0 = q < kPPW ? row0 : col0;
+    const int ld = q < kPPW ? ldp : ldq;
+    const int r0 = q < kPPW ? row0 : col0;
+    if (!(q < kPPW ? kPT : kUpd)) {
       const int row = u >> 2, c = (u & 3) ^ kswz(row);
       doff[q] = static_cast<uint32_t>((static_cast<size_t>(r0 + row) * ld + c * V) * sizeof(S));
     } else {
       constexpr int UPR = kTile / V;    // 16-byte chunks per k-row
       const int kk = u / UPR, pc = u % UPR;
       const int c = (V == 8) ? (pc ^ (4 * (kk & 3))) : pc;
-      doff[q] = static_cast<uint32_t>((static_cast<size_t>(kk) * ldq + col0 + c * V) * sizeof(S));
+      doff[q] = static_cast<uint32_t>((static_cast<size_t>(kk) * ld + r0 + c * V) * sizeof(S));
     }
   }
   // Every DMA destination is a link-time constant (the stage object and the
@@ -392,7 +399,7 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
     const uint4* sbuf = stage == 0 ? st0 : stage == 1 ? st1 : stage == 2 ? st2 : st3;
     const char* base;
     if (q < kPPW)
-      base = reinterpret_cast<const char*>(P + k0);
+      base = reinterpret_cast<const char*>(kPT ? P + static_cast<size_t>(k0) * ldp : P + k0);
     else if (!kUpd)
       base = reinterpret_cast<const char*>(Q + k0);
     else
@@ -407,44 +414,52 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
   // (bf16: K = 8*(2s + l/32) .. +8) of output row l%32 of each 32-row block.
   // Read piece p: 0..3 the P fragments fa[i]; then the Q fragments (NT: one
   // piece per fb[j]; bf16 update: two transposing reads per fb[j]).
-  constexpr int kReadPieces = (kUpd && V == 8) ? 4 + 2 * kBJ : 4 + kBJ;
-  static_assert(kReadPieces <= kSlots, "one fragment read per MFMA slot at most");
+  constexpr int kPReads = kPT ? 8 : 4;
+  constexpr int kReadPieces = kPReads + ((kUpd && V == 8) ? 2 * kBJ : kBJ);
+  // Transposing read of half r of the fragment of a K-strided bf16 panel
+  // whose 32 columns start at n_base: within each 16-lane group, lane i points
+  // at k-row kb + i/4, columns n0 + 4*(i%4) .. +4; lane j receives column
+  // n0 + j at k-rows kb .. kb+3.
+  auto tr_read = [&](const uint4* panel, int s, int n_base, int r, uint4& f) {
+    const int il = lane & 15;
+    const int n = n_base + 16 * ((lane >> 4) & 1) + 4 * (il & 3);
+    const int kk = 16 * s + 8 * lhalf + 4 * r + (il >> 2);
+    const int byte = kk * 512 + (((n >> 3) ^ (4 * (kk & 3))) << 4) + ((n & 7) << 1);
+    const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MFSDP_LDS v4i16_t*)(reinterpret_cast<const char*>(panel) + byte));
+    const uint32_t w0 = static_cast<uint16_t>(t[0]) |
+                        (static_cast<uint32_t>(static_cast<uint16_t>(t[1])) << 16);
+    const uint32_t w1 = static_cast<uint16_t>(t[2]) |
+                        (static_cast<uint32_t>(static_cast<uint16_t>(t[3])) << 16);
+    if (r == 0) {
+      f.x = w0;
+      f.y = w1;
+    } else {
+      f.z = w0;
+      f.w = w1;
+    }
+  };
   auto read_piece = [&](const uint4* buf, int s, int p, uint4 (&fa)[4], uint4 (&fb)[kBJ]) {
     const int c = 2 * s + lhalf;
-    if (p < 4) {
-      const int row = wr * 128 + p * 32 + lrow;
-      fa[p] = buf[row * 4 + (c ^ kswz(row))];
+    if (p < kPReads) {
+      if constexpr (kPT) {
+        tr_read(buf, s, wr * 128 + (p >> 1) * 32, p & 1, fa[p >> 1]);
+      } else {
+        const int row = wr * 128 + p * 32 + lrow;
+        fa[p] = buf[row * 4 + (c ^ kswz(row))];
+      }
       return;
     }
     const uint4* qp = buf + PANEL;
+    const int q = p - kPReads;
     if constexpr (!kUpd) {
-      const int j = p - 4;
+      const int j = q;
       const int row = wc * kWaveCols + j * 32 + lrow;
       fb[j] = qp[row * 4 + (c ^ kswz(row))];
     } else if constexpr (V == 8) {
-      // Transposing read: within each 16-lane group, lane i points at k-row
-      // kb + i/4, columns n0 + 4*(i%4) .. +4; lane j receives column n0 + j
-      // at k-rows kb .. kb+3.
-      const int j = (p - 4) >> 1, r = (p - 4) & 1;
-      const int il = lane & 15;
-      const int n = wc * kWaveCols + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (il & 3);
-      const int kk = 16 * s + 8 * lhalf + 4 * r + (il >> 2);
-      const int byte = kk * 512 + (((n >> 3) ^ (4 * (kk & 3))) << 4) + ((n & 7) << 1);
-      const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (MFSDP_LDS v4i16_t*)(reinterpret_cast<const char*>(qp) + byte));
-      const uint32_t w0 = static_cast<uint16_t>(t[0]) |
-                          (static_cast<uint32_t>(static_cast<uint16_t>(t[1])) << 16);
-      const uint32_t w1 = static_cast<uint16_t>(t[2]) |
-                          (static_cast<uint32_t>(static_cast<uint16_t>(t[3])) << 16);
-      if (r == 0) {
-        fb[j].x = w0;
-        fb[j].y = w1;
-      } else {
-        fb[j].z = w0;
-        fb[j].w = w1;
-      }
+      tr_read(qp, s, wc * kWaveCols + (q >> 1) * 32, q & 1, fb[q >> 1]);
     } else {
-      const int j = p - 4;
+      const int j = q;
       const float* qf = reinterpret_cast<const float*>(qp);
       const int n = wc * kWaveCols + j * 32 + lrow;
       const int kk = 4 * c;
@@ -464,8 +479,9 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
   uint4 fa[2][4], fb[2][kBJ];
 
   // One K step t on stage buffer X.  Sub-step 0 issues its kSlots MFMAs one per
-  // slot; each slot also issues one fragment read of sub-step 1 and (when
-  // DMA) one DMA piece of step t + kStages - 1 into stage Y, the buffer of
+  // slot; slot idx also issues fragment reads idx, idx + kSlots, ... of
+  // sub-step 1 and (every fourth slot, when DMA) one DMA piece of step
+  // t + kStages - 1 into stage Y, the buffer of
   // step t - 1.  Then: wait until the DMA of step t + 1 has landed (the two
   // most recent steps' DMAs may stay in flight), block barrier.  Sub-step 1's
   // MFMAs overlap the fragment reads of step t + 1 from stage N.
@@ -479,7 +495,8 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
 #pragma unroll
     for (int idx = 0; idx < kSlots; ++idx) {
       Mma<E>::run(acc[idx / kBJ][idx % kBJ], fa[0][idx / kBJ], fb[0][idx % kBJ]);
-      if (idx < kReadPieces) read_piece(X, 1, idx, fa[1], fb[1]);
+#pragma unroll
+      for (int rp = idx; rp < kReadPieces; rp += kSlots) read_piece(X, 1, rp, fa[1], fb[1]);
       if constexpr (do_dma) {
         if (dma_slot_piece(kBJ, 0, idx) >= 0) dma_piece(Y, k_dma, dma_slot_piece(kBJ, 0, idx));
       }
@@ -502,7 +519,8 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
     for (int idx = 0; idx < kSlots; ++idx) {
       Mma<E>::run(acc[idx / kBJ][idx % kBJ], fa[1][idx / kBJ], fb[1][idx % kBJ]);
       if constexpr (has_next) {
-        if (idx < kReadPieces) read_piece(N, 0, idx, fa[0], fb[0]);
+#pragma unroll
+        for (int rp = idx; rp < kReadPieces; rp += kSlots) read_piece(N, 0, rp, fa[0], fb[0]);
       }
       if constexpr (do_dma) {
         if (dma_slot_piece(kBJ, 1, idx) >= 0) dma_piece(Y, k_dma, dma_slot_piece(kBJ, 1, idx));
