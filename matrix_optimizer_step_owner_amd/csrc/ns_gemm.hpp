@@ -363,8 +363,11 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
   // B'[k0..+32, row0..+256], 32 rows of 512 contiguous bytes.  Each DMA
   // request then covers whole 128-byte lines instead of 64-byte halves, which
   // halves the L1-to-L2 requests of that panel: the texture path that feeds
-  // these DMAs is the busiest unit of the K loop on long-K products.
-  constexpr bool kPT = kUpd && V == 8;
+  // these DMAs is the busiest unit of the K loop on long-K products.  The
+  // polynomial's operands are both panels of the symmetric A, so in bf16 it
+  // reads both as column panels.
+  constexpr bool kPT = (kUpd || MODE == kModePoly) && V == 8;   // P panel K-strided
+  constexpr bool kQT = kUpd || (MODE == kModePoly && V == 8);   // Q panel K-strided
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> kWaveRowLog2, wc = wave & (kNsWaves / 2 - 1);
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
     const int u = wave * (kPPW * 64) + (q % kPPW) * 64 + lane;
     const int ld = q < kPPW ? ldp : ldq;
     const int r0 = q < kPPW ? row0 : col0;
-    if (!(q < kPPW ? kPT : kUpd)) {
+    if (!(q < kPPW ? kPT : kQT)) {
       const int row = u >> 2, c = (u & 3) ^ kswz(row);
       doff[q] = static_cast<uint32_t>((static_cast<size_t>(r0 + row) * ld + c * V) * sizeof(S));
     } else {
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
     const char* base;
     if (q < kPPW)
       base = reinterpret_cast<const char*>(kPT ? P + static_cast<size_t>(k0) * ldp : P + k0);
-    else if (!kUpd)
+    else if (!kQT)
       base = reinterpret_cast<const char*>(Q + k0);
     else
       base = reinterpret_cast<const char*>(Q + static_cast<size_t>(k0) * ldq);
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
   // Read piece p: 0..3 the P fragments fa[i]; then the Q fragments (NT: one
   // piece per fb[j]; bf16 update: two transposing reads per fb[j]).
   constexpr int kPReads = kPT ? 8 : 4;
-  constexpr int kReadPieces = kPReads + ((kUpd && V == 8) ? 2 * kBJ : kBJ);
+  constexpr int kReadPieces = kPReads + ((kQT && V == 8) ? 2 * kBJ : kBJ);
   // Transposing read of half r of the fragment of a K-strided bf16 panel
   // whose 32 columns start at n_base: within each 16-lane group, lane i points
   // at k-row kb + i/4, columns n0 + 4*(i%4) .. +4; lane j receives column
@@ -452,7 +455,7 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
     }
     const uint4* qp = buf + PANEL;
     const int q = p - kPReads;
-    if constexpr (!kUpd) {
+    if constexpr (!kQT) {
       const int j = q;
       const int row = wc * kWaveCols + j * 32 + lrow;
       fb[j] = qp[row * 4 + (c ^ kswz(row))];
