@@ -159,6 +159,23 @@ struct Vec16<ElemF32> {
   }
 };
 
+// Element offset of (r, c) in a Newton-Schulz iterate of row length n_pad
+// (a multiple of 256; m_pad too).  bf16 iterates are stored in blocks of 256
+// rows x 32 columns (16 KB, row-major inside), block (r / 256, c / 32) at
+// ((r / 256) * (n_pad / 32) + c / 32) * 8192: one K step of a 256-row Gram
+// panel is then one contiguous block, and 32 rows of one column block are 2 KB
+// contiguous, so every DMA request of the Gram and update operands covers
+// whole 128-byte lines.  Eight consecutive columns from a multiple of eight
+// stay contiguous (16-byte vectors).  fp32 iterates are row-major.
+template <class E>
+__host__ __device__ __forceinline__ size_t iter_off(int64_t r, int64_t c, int64_t n_pad) {
+  if constexpr (E::kVec == 8)
+    return static_cast<size_t>((((r >> 8) * (n_pad >> 5) + (c >> 5)) << 13) + ((r & 255) << 5) +
+                               (c & 31));
+  else
+    return static_cast<size_t>(r * n_pad + c);
+}
+
 // Per-matrix device descriptor, written by the host into the workspace.
 // "Wide" coordinates (i < m, j < n) index the Newton-Schulz iterate; a tall
 // matrix (rows > cols) maps wide (i, j) to stored (j, i).
@@ -167,8 +184,8 @@ struct MatDesc {
   const void* G;      // rows x cols
   void* M;            // rows x cols
   float* upd;         // rows x cols fp32 or null
-  void* X0;           // m_pad x n_pad: U, then even iterates
-  void* X1;           // m_pad x n_pad: odd iterates
+  void* X0;           // m_pad x n_pad (iter_off layout): U, then even iterates
+  void* X1;           // m_pad x n_pad (iter_off layout): odd iterates
   void* A;            // m_pad x m_pad: X X^T
   void* B;            // m_pad x m_pad: b A + c A A
   int32_t rows, cols;

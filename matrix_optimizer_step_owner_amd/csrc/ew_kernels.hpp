@@ -10,7 +10,8 @@
 namespace mfsdp {
 
 // Momentum M' = beta*M + G, Nesterov U = G + beta*M' (or U = M'), sum of U^2
-// per block, and U stored into X0 in wide layout (transposed when rows > cols),
+// per block, and U stored into X0 in wide layout (transposed when rows > cols;
+// iter_off addressing),
 // zero in the tile padding.  A block is 64 stored rows x 128 stored columns
 // (kEwRows x kEwCols) and owns one partial sum of U^2; one 256-thread
 // workgroup covers kEwSub consecutive blocks of one matrix, with every load of
@@ -121,8 +122,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
           row[2] = pk.z;
           row[3] = pk.w;
         } else {  // same layout: straight to X0
-          gst_stream(X0 + static_cast<size_t>(i0s[q] + r) * d.n_pad + j0s[q] + cv * V,
-                     Vec16<E>::pack(u));
+          gst_stream(X0 + iter_off<E>(i0s[q] + r, j0s[q] + cv * V, d.n_pad), Vec16<E>::pack(u));
         }
       }
     }
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
   }
   __syncthreads();
 
-  // Store U into X0 (wide layout, rows 16-byte aligned, padding included):
+  // Store U into X0 (wide layout, iter_off addressing, padding included):
   // wide row ii of a block is stored row ii (wide) or stored column ii (tall).
   // The vector path of a wide matrix has already stored it.
   for (int q = 0; q < nsub; ++q) {
@@ -158,8 +158,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
         S w[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) w[k] = sU[q][ii][jv * V + k];
-        gst_stream(X0 + static_cast<size_t>(i0s[q] + ii) * d.n_pad + j0s[q] + jv * V,
-                   pack_raw(w));
+        gst_stream(X0 + iter_off<E>(i0s[q] + ii, j0s[q] + jv * V, d.n_pad), pack_raw(w));
       }
     } else if (d.tall) {
       constexpr int VPR = SR / V;
@@ -168,8 +167,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(
         S w[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) w[k] = sU[q][jv * V + k][ii];
-        gst_stream(X0 + static_cast<size_t>(i0s[q] + ii) * d.n_pad + j0s[q] + jv * V,
-                   pack_raw(w));
+        gst_stream(X0 + iter_off<E>(i0s[q] + ii, j0s[q] + jv * V, d.n_pad), pack_raw(w));
       }
     }
   }
@@ -227,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void apply_x0_kernel(
   for (int e = threadIdx.x; e < d.ew_th * d.ew_tw; e += kThreads) {
     const int i = i0 + e / d.ew_tw, j = j0 + e % d.ew_tw;
     if (i >= d.m || j >= d.n) continue;
-    const float o = s * E::to_f32(X0[static_cast<size_t>(i) * d.n_pad + j]);
+    const float o = s * E::to_f32(X0[iter_off<E>(i, j, d.n_pad)]);
     const size_t off = d.tall ? static_cast<size_t>(j) * d.cols + i
                               : static_cast<size_t>(i) * d.cols + j;
     W[off] = E::from_f32(fmaf(-d.lr_scale, o, decay * E::to_f32(W[off])));

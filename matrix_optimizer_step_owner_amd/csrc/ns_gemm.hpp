@@ -368,6 +368,12 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
   // reads both as column panels.
   constexpr bool kPT = (kUpd || MODE == kModePoly) && V == 8;   // P panel K-strided
   constexpr bool kQT = kUpd || (MODE == kModePoly && V == 8);   // Q panel K-strided
+  // bf16 iterates are blocked (iter_off): a K step of a Gram panel is one
+  // contiguous 16 KB block, and the update's X panel is eight 2 KB runs, one
+  // per 32-column block, kept in that order in LDS (chunk-major: column block
+  // cb, k-row kk, 16-byte unit u at cb*2048 + kk*64 + u*16).
+  constexpr bool kGB = (MODE == kModeGram || MODE == kModeSyrk) && V == 8;
+  constexpr bool kUB = kUpd && V == 8;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> kWaveRowLog2, wc = wave & (kNsWaves / 2 - 1);
@@ -384,7 +390,13 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
     const int u = wave * (kPPW * 64) + (q % kPPW) * 64 + lane;
     const int ld = q < kPPW ? ldp : ldq;
     const int r0 = q < kPPW ? row0 : col0;
-    if (!(q < kPPW ? kPT : kQT)) {
+    if (kGB) {
+      const int row = u >> 2, c = (u & 3) ^ kswz(row);
+      doff[q] = static_cast<uint32_t>(((row << 5) + c * V) * sizeof(S));
+    } else if (q >= kPPW && kUB) {
+      const int cb = u >> 7, kk = (u >> 2) & 31, c = u & 3;
+      doff[q] = static_cast<uint32_t>(((cb << 13) + (kk << 5) + c * V) * sizeof(S));
+    } else if (!(q < kPPW ? kPT : kQT)) {
       const int row = u >> 2, c = (u & 3) ^ kswz(row);
       doff[q] = static_cast<uint32_t>((static_cast<size_t>(r0 + row) * ld + c * V) * sizeof(S));
     } else {
@@ -400,11 +412,20 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
   auto dma_piece = [&](auto stage_c, int k0, int q) {
     constexpr int stage = decltype(stage_c)::value;
     const uint4* sbuf = stage == 0 ? st0 : stage == 1 ? st1 : stage == 2 ? st2 : st3;
+    // block (r / 256, c / 32) of a blocked iterate with row length ld
+    auto blk = [](int r, int c, int ld) {
+      return static_cast<size_t>((r >> 8) * (ld >> 5) + (c >> 5)) << 13;
+    };
     const char* base;
-    if (q < kPPW)
+    if (kGB)
+      base = reinterpret_cast<const char*>((q < kPPW ? P : Q) +
+                                           blk(q < kPPW ? row0 : col0, k0, q < kPPW ? ldp : ldq));
+    else if (q < kPPW)
       base = reinterpret_cast<const char*>(kPT ? P + static_cast<size_t>(k0) * ldp : P + k0);
     else if (!kQT)
       base = reinterpret_cast<const char*>(Q + k0);
+    else if (kUB)
+      base = reinterpret_cast<const char*>(Q + blk(k0, col0, ldq) + ((k0 & 255) << 5));
     else
       base = reinterpret_cast<const char*>(Q + static_cast<size_t>(k0) * ldq);
     const uint32_t dst = lds_addr(sbuf) + wave_off + (q < kPPW ? 0u : PANEL * 16u) +
@@ -423,11 +444,17 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
   // whose 32 columns start at n_base: within each 16-lane group, lane i points
   // at k-row kb + i/4, columns n0 + 4*(i%4) .. +4; lane j receives column
   // n0 + j at k-rows kb .. kb+3.
-  auto tr_read = [&](const uint4* panel, int s, int n_base, int r, uint4& f) {
+  // k-row-major panels (a row-major source: 512-byte k-rows, 16-byte units
+  // XOR-swizzled by 4*(kk & 3)) or chunk-major ones (the blocked iterate of
+  // the update; consecutive k-rows of a column block are 64 bytes apart and
+  // need no swizzle).
+  auto tr_read = [&](const uint4* panel, int s, int n_base, int r, uint4& f, auto chunk_c) {
+    constexpr bool chunk = decltype(chunk_c)::value;
     const int il = lane & 15;
     const int n = n_base + 16 * ((lane >> 4) & 1) + 4 * (il & 3);
     const int kk = 16 * s + 8 * lhalf + 4 * r + (il >> 2);
-    const int byte = kk * 512 + (((n >> 3) ^ (4 * (kk & 3))) << 4) + ((n & 7) << 1);
+    const int byte = chunk ? (n >> 5) * 2048 + kk * 64 + (((n >> 3) & 3) << 4) + ((n & 7) << 1)
+                           : kk * 512 + (((n >> 3) ^ (4 * (kk & 3))) << 4) + ((n & 7) << 1);
     const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (MFSDP_LDS v4i16_t*)(reinterpret_cast<const char*>(panel) + byte));
     const uint32_t w0 = static_cast<uint16_t>(t[0]) |
@@ -446,7 +473,8 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
     const int c = 2 * s + lhalf;
     if (p < kPReads) {
       if constexpr (kPT) {
-        tr_read(buf, s, wr * 128 + (p >> 1) * 32, p & 1, fa[p >> 1]);
+        tr_read(buf, s, wr * 128 + (p >> 1) * 32, p & 1, fa[p >> 1],
+                std::integral_constant<bool, false>{});
       } else {
         const int row = wr * 128 + p * 32 + lrow;
         fa[p] = buf[row * 4 + (c ^ kswz(row))];
@@ -460,7 +488,8 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
       const int row = wc * kWaveCols + j * 32 + lrow;
       fb[j] = qp[row * 4 + (c ^ kswz(row))];
     } else if constexpr (V == 8) {
-      tr_read(qp, s, wc * kWaveCols + (q >> 1) * 32, q & 1, fb[q >> 1]);
+      tr_read(qp, s, wc * kWaveCols + (q >> 1) * 32, q & 1, fb[q >> 1],
+              std::integral_constant<bool, kUB>{});
     } else {
       const int j = q;
       const float* qf = reinterpret_cast<const float*>(qp);
@@ -640,7 +669,8 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
       int grow, gcol, sl, r_in, c_in;
       coordA(i, p, grow, gcol, sl, r_in, c_in);
       if (MODE != kModeGram && MODE != kModeSyrk && !(kUpd && ep.fold))
-        xin[p] = load_raw8<E>(ein + static_cast<size_t>(grow) * ldo + gcol);
+        xin[p] = load_raw8<E>(ein + (kUpd ? iter_off<E>(grow, gcol, ldo)
+                                          : static_cast<size_t>(grow) * ldo + gcol));
       if (wide_apply && vec && grow < d.m && gcol + 8 <= d.n)
         win[p] = load_raw8<E>(W + static_cast<size_t>(grow) * d.cols + gcol);
       if constexpr (tall_apply && V == 8) {   // fp32: loaded in pass B (registers)
@@ -671,7 +701,8 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
       const float4 lo = *reinterpret_cast<const float4*>(src_lo);
       const float4 hi = *reinterpret_cast<const float4*>(src_hi);
       float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      const size_t goff = static_cast<size_t>(grow) * ldo + gcol;
+      const size_t goff = kUpd ? iter_off<E>(grow, gcol, ldo)
+                               : static_cast<size_t>(grow) * ldo + gcol;
       if (MODE == kModeGram) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= alpha;

@@ -174,7 +174,7 @@ __device__ __forceinline__ void small_update(lds_float* X, int px, const lds_flo
 }
 
 // One workgroup per small matrix: the whole Newton-Schulz chain and the apply.
-// The iterate X0 holds U (wide layout, row pitch n_pad) from the momentum
+// The iterate X0 holds U (wide layout, iter_off addressing) from the momentum
 // kernel; scales[k] = 1 / (||U||_F + eps).
 template <class E>
 __global__ __launch_bounds__(kSmallThreads) void small_ns_kernel(
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_ns_kernel(
   const S* X0 = static_cast<const S*>(d.X0);
   for (int e = threadIdx.x; e < m * n; e += kSmallThreads) {
     const int i = e / n, j = e % n;
-    X[i * px + j] = E::to_f32(gld<S>(X0 + static_cast<size_t>(i) * d.n_pad + j));
+    X[i * px + j] = E::to_f32(gld<S>(X0 + iter_off<E>(i, j, d.n_pad)));
   }
   __syncthreads();
   for (int it = 0; it < args.ns_steps; ++it) {

@@ -1,8 +1,9 @@
 // Preparation of a gradient for its preconditioner statistics (Shampoo-type
 // L = G G^T and R = G^T G): G (rows x cols, storage dtype, row-major) is
 // copied into the workspace twice, as Xg (r_pad x c_pad) and as its transpose
-// Xt (c_pad x r_pad), zero outside G, so that both statistics are Gram
-// products of a 256-padded operand (kModeSyrk of ns_gemm_kernel).
+// Xt (c_pad x r_pad), both in iter_off layout, zero outside G, so that both
+// statistics are Gram products of a 256-padded operand (kModeSyrk of
+// ns_gemm_kernel).
 #pragma once
 
 #include "common.hpp"
@@ -31,13 +32,13 @@ __global__ __launch_bounds__(kThreads) void stats_prep_kernel(const MatDesc* __r
     const int r = e / T, c = e % T;
     const int gr = r0 + r, gc = c0 + c;
     const S v = (gr < d.rows && gc < d.cols) ? G[static_cast<size_t>(gr) * d.cols + gc] : zero;
-    Xg[static_cast<size_t>(gr) * d.n_pad + gc] = v;
+    Xg[iter_off<E>(gr, gc, d.n_pad)] = v;
     sT[r][c] = v;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < T * T; e += kThreads) {
     const int c = e / T, r = e % T;
-    Xt[static_cast<size_t>(c0 + c) * d.m_pad + r0 + r] = sT[r][c];
+    Xt[iter_off<E>(c0 + c, r0 + r, d.m_pad)] = sT[r][c];
   }
 }
 
