@@ -436,20 +436,20 @@ hipError_t enqueue_ns_group(const Plan& p, const Plan::Group& gr, const MatDesc*
     ep.kb = skip_poly ? b : 1.f;
     ep.decay = decay;
     e = launch(MFSDP_KERNEL_GRAM, stream, [&] {
-      ns_gemm_kernel<E, kModeGram><<<dim3(static_cast<unsigned>(gr.sym)), dim3(ns_threads(kModeGram)), 0,
+      ns_gemm_kernel<E, kModeGram><<<dim3(static_cast<unsigned>(gr.sym)), dim3(kNsThreads), 0,
                                      stream>>>(descs, tiles + gr.t_sym, scales, ep);
     });
     if (e != hipSuccess) return e;
     if (!skip_poly) {
       e = launch(MFSDP_KERNEL_POLY, stream, [&] {
-        ns_gemm_kernel<E, kModePoly><<<dim3(static_cast<unsigned>(gr.sym)), dim3(ns_threads(kModePoly)), 0,
+        ns_gemm_kernel<E, kModePoly><<<dim3(static_cast<unsigned>(gr.sym)), dim3(kNsThreads), 0,
                                        stream>>>(descs, tiles + gr.t_sym, scales, ep);
       });
       if (e != hipSuccess) return e;
     }
     if (it + 1 < ns_steps) {
       e = launch(MFSDP_KERNEL_UPDATE, stream, [&] {
-        ns_gemm_kernel<E, kModeUpdate><<<dim3(static_cast<unsigned>(gr.upd)), dim3(ns_threads(kModeUpdate)), 0,
+        ns_gemm_kernel<E, kModeUpdate><<<dim3(static_cast<unsigned>(gr.upd)), dim3(kNsThreads), 0,
                                          stream>>>(descs, tiles + gr.t_upd, scales, ep);
       });
       if (e != hipSuccess) return e;
@@ -457,7 +457,7 @@ hipError_t enqueue_ns_group(const Plan& p, const Plan::Group& gr, const MatDesc*
       if (gr.fin_wide > 0) {
         e = launch(MFSDP_KERNEL_FINAL, stream, [&] {
           ns_gemm_kernel<E, kModeApplyWide><<<dim3(static_cast<unsigned>(gr.fin_wide)),
-                                              dim3(ns_threads(kModeApplyWide)), 0, stream>>>(
+                                              dim3(kNsThreads), 0, stream>>>(
               descs, tiles + gr.t_fin_wide, scales, ep);
         });
         if (e != hipSuccess) return e;
@@ -465,7 +465,7 @@ hipError_t enqueue_ns_group(const Plan& p, const Plan::Group& gr, const MatDesc*
       if (gr.fin_tall > 0) {
         e = launch(MFSDP_KERNEL_FINAL, stream, [&] {
           ns_gemm_kernel<E, kModeApplyTall><<<dim3(static_cast<unsigned>(gr.fin_tall)),
-                                              dim3(ns_threads(kModeApplyTall)), 0, stream>>>(
+                                              dim3(kNsThreads), 0, stream>>>(
               descs, tiles + gr.t_fin_tall, scales, ep);
         });
         if (e != hipSuccess) return e;
@@ -652,7 +652,7 @@ hipError_t enqueue_stats(const StatsPlan& p, int64_t n, char* ws, float alpha, f
   ep.a = alpha;
   ep.b = beta;
   return launch(MFSDP_KERNEL_SYRK, stream, [&] {
-    ns_gemm_kernel<E, kModeSyrk><<<dim3(static_cast<unsigned>(p.syrk_tiles)), dim3(ns_threads(kModeSyrk)), 0,
+    ns_gemm_kernel<E, kModeSyrk><<<dim3(static_cast<unsigned>(p.syrk_tiles)), dim3(kNsThreads), 0,
                                    stream>>>(syrk, reinterpret_cast<const int2*>(ws + p.off_tiles),
                                              reinterpret_cast<const float*>(ws + p.off_scales),
                                              ep);

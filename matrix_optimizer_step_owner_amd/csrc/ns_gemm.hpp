@@ -9,9 +9,8 @@
 // first gram uses the un-normalized U with alpha = s^2 and the first update
 // alpha = s, where s = 1 / (||U||_F + eps).
 //
-// Kernel shape: one workgroup per 256x256 output tile, of 4 waves (each a
-// 128x128 quadrant of 4x4 MFMA 32x32 blocks; the Gram products) or 8 waves
-// (each 128x64, 4x2 blocks; the other products).  Operand panels (one K step: 64
+// Kernel shape: one workgroup per 256x256 output tile, 8 waves, each a
+// 128x64 block of 4x2 MFMA 32x32 tiles.  Operand panels (one K step: 64
 // bf16 or 32 fp32 per row) go from global memory straight into LDS
 // (global_load_lds_dwordx4, no register staging) in four 32 KB stages;
 // rows are XOR-swizzled in 16-byte chunks so fragment reads are free of bank
@@ -246,33 +245,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // chunk, which (row >> 2) & 3 spreads over all 16 bank groups.
 __device__ __forceinline__ int kswz(int row) { return (row >> 2) & 3; }
 
-// Waves per 256x256 tile: 4 (one per SIMD, each wave a 128 x 128 quadrant,
-// 256 accumulator registers) or 8 (two per SIMD, each wave 128 x 64, 128
-// accumulator registers).  With two waves per SIMD, one wave's epilogue
-// loads, LDS staging and stores overlap the other's: the polynomial, update
-// and apply launches run 1-11% faster with 8 waves.  The Gram products (and
-// the statistics product) keep 4: their K loops are the longest and the NT
-// fragment reads of 128 x 64 wave tiles (six per eight MFMAs instead of eight
-// per sixteen) made them 3-6% slower.
-__host__ __device__ constexpr int ns_waves(int mode) {
-  return (mode == kModeGram || mode == kModeSyrk) ? 4 : 8;
-}
-__host__ __device__ constexpr int ns_threads(int mode) { return 64 * ns_waves(mode); }
-
-template <int W>
-struct NsShape {
-  static_assert(W == 4 || W == 8, "4 or 8 waves per tile");
-  static constexpr int kThreads = 64 * W;
-  static constexpr int kWaveCols = 2 * kTile / W;       // output columns per wave
-  static constexpr int kWaveColsLog2 = W == 8 ? 6 : 7;
-  static constexpr int kWaveRowLog2 = W == 8 ? 2 : 1;   // wave index -> 128-row half
-  static_assert(kWaveCols == 1 << kWaveColsLog2 && W / 2 == 1 << kWaveRowLog2, "powers of two");
-  static constexpr int kBJ = kWaveCols / 32;            // 32-column MFMA blocks per wave
-  static constexpr int kSlots = 4 * kBJ;                // MFMAs per wave per K sub-step
-  static constexpr int kPieces = 32 / W;                // 1 KB DMA pieces per wave per K step
-  static constexpr int kPPW = kPieces / 2;              // of them per operand panel
-  static constexpr int kEpIt = 64 * kTile / 8 / kThreads;   // epilogue 8-element groups per thread
-};
+// Eight waves per 256x256 tile, two per SIMD, each wave a 128 x 64 block of
+// 4x2 MFMA 32x32 tiles (128 accumulator registers, ~250 VGPRs in all).  With
+// two waves per SIMD, one wave's stalls (an LDS instruction it cannot issue
+// yet, its epilogue loads, staging and stores) leave the MFMA pipe to the
+// other.
+constexpr int kNsWaves = 8;
+constexpr int kNsThreads = 64 * kNsWaves;
+constexpr int kWaveCols = 2 * kTile / kNsWaves;   // 64 output columns per wave
+constexpr int kWaveColsLog2 = 6;
+constexpr int kWaveRowLog2 = 2;                   // wave index -> 128-row half
+static_assert(kWaveCols == 1 << kWaveColsLog2 && kNsWaves / 2 == 1 << kWaveRowLog2, "powers of two");
+constexpr int kBJ = kWaveCols / 32;               // 32-column MFMA blocks per wave
+constexpr int kSlots = 4 * kBJ;                   // MFMAs per wave per K sub-step
+constexpr int kPieces = 32 / kNsWaves;            // 1 KB DMA pieces per wave per K step
+constexpr int kPPW = kPieces / 2;                 // of them per operand panel
+constexpr int kEpIt = 64 * kTile / 8 / kNsThreads;   // epilogue 8-element groups per thread
 
 // Which DMA piece (0..2*bj-1, or -1 for none) a K step issues in MFMA slot
 // idx of sub-step sub, for waves with bj 32-column blocks: the pieces of a
@@ -289,7 +277,7 @@ __host__ __device__ constexpr int dma_slot_piece(int bj, int sub, int idx) {
 constexpr int kUpdBandRows = 4;
 
 template <class E, int MODE>
-__global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
+__global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
     const MatDesc* __restrict__ descs, const int2* __restrict__ tiles,
     const float* __restrict__ scales, NsEpi ep) {
   using S = typename E::storage_t;
@@ -297,13 +285,6 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
   constexpr int BK = 4 * V;             // K elements per 64-byte panel row
   constexpr int PANEL = kTile * 4;      // uint4 per operand panel (16 KB)
   constexpr int kStages = 4;            // LDS pipeline depth (4 x 32 KB)
-  using SH = NsShape<ns_waves(MODE)>;
-  constexpr int kNsWaves = ns_waves(MODE);
-  constexpr int kNsThreads = SH::kThreads;
-  constexpr int kWaveCols = SH::kWaveCols, kWaveColsLog2 = SH::kWaveColsLog2;
-  constexpr int kWaveRowLog2 = SH::kWaveRowLog2;
-  constexpr int kBJ = SH::kBJ, kSlots = SH::kSlots;
-  constexpr int kPieces = SH::kPieces, kPPW = SH::kPPW, kEpIt = SH::kEpIt;
 
   // Pipeline stages, each holding the P panel then the Q panel.  Separate
   // objects so that the compiler can tell a DMA into one stage from reads of
@@ -540,11 +521,9 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
     // DMAs that may stay in flight at the barrier of step t: the kPieces of
     // step t - 1 and the half that step t issued before its barrier (step
     // t + 1's must be done).
-    static_assert(kPieces == 8 || kPieces == 4, "wait counts below");
+    static_assert(kPieces == 4, "wait count below: 4 + 2 pieces in flight");
     if constexpr (wait_all)
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (kPieces == 8)
-      asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
@@ -576,11 +555,8 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
   for (int q = 0; q < kPieces; ++q) dma_piece(S1{}, BK, q);
 #pragma unroll
   for (int q = 0; q < kPieces; ++q) dma_piece(S2{}, 2 * BK, q);
-  // the two later stages may stay in flight
-  if constexpr (kPieces == 8)
-    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // the two later stages (2 x kPieces) may stay in flight
+  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int p = 0; p < kReadPieces; ++p) read_piece(st0, 0, p, fa[0], fb[0]);
   int t = 0;
@@ -609,7 +585,7 @@ __global__ __launch_bounds__(ns_threads(MODE)) void ns_gemm_kernel(
   constexpr int SP = kWaveCols;         // staged row pitch in floats
   // column c of staged row r lives at r*SP + (c ^ 4*((r >> 2) & 7))
   auto sidx = [](int r, int c) { return r * SP + (c ^ (((r >> 2) & 7) << 2)); };
-  // wave slice w (32 x kWaveCols floats: 16 or 8 KB) lives in stage array
+  // wave slice w (32 x kWaveCols floats, 8 KB) lives in stage array
   // w / kPer, at slice w % kPer of its 32 KB
   constexpr int kPer = kNsWaves / 4;
   auto slice_of = [&](int w) -> float* {

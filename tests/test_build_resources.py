@@ -1,7 +1,7 @@
 """Resource guards of the gfx950 kernels (host-side compile, no GPU).
 
-The Newton-Schulz kernels must keep their 256 fp32 accumulators and their
-epilogue inputs in registers (no scratch: a dynamically indexed accumulator
+The Newton-Schulz kernels must keep their 128 fp32 accumulators per wave and
+their epilogue inputs in registers (no scratch: a dynamically indexed accumulator
 array, a spill, or an array passed by reference to an outlined helper moves
 to scratch memory and costs several times in speed) and stay well inside the
 64 KB instruction cache that two CUs share (the once-per-tile epilogue is
