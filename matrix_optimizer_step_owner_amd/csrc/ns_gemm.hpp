@@ -585,13 +585,14 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
   constexpr int SP = kWaveCols;         // staged row pitch in floats
   // column c of staged row r lives at r*SP + (c ^ 4*((r >> 2) & 7))
   auto sidx = [](int r, int c) { return r * SP + (c ^ (((r >> 2) & 7) << 2)); };
-  // wave slice w (32 x kWaveCols floats, 8 KB) lives in stage array
-  // w / kPer, at slice w % kPer of its 32 KB
-  constexpr int kPer = kNsWaves / 4;
-  auto slice_of = [&](int w) -> float* {
-    const int sa = w / kPer;
+  // Two staging halves h = 0, 1, so that block i + 1 is staged while block i
+  // is stored: wave slice w (32 x kWaveCols floats, 8 KB) of half h lives in
+  // stage array w / 2, at byte offset (w % 2) * 8 KB + h * 16 KB of its 32 KB.
+  static_assert(kNsWaves == 8 && 32 * kWaveCols * 4 == 8192, "two 8 KB slices per half stage");
+  auto slice_of = [&](int w, int h) -> float* {
+    const int sa = w >> 1;
     float* b = reinterpret_cast<float*>(sa == 0 ? st0 : sa == 1 ? st1 : sa == 2 ? st2 : st3);
-    return b + (w % kPer) * (32 * kWaveCols);
+    return b + (w & 1) * (32 * kWaveCols) + h * (64 * kWaveCols);
   };
   const float s_norm = scales[k];
   constexpr bool sym = !kUpd;
@@ -619,8 +620,6 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
     gcol = col0 + col;
   };
 
-  // One 64 x 256 block per accumulator row i; i is a compile-time constant
-  // so that acc stays in registers.
   // pass B coordinates of iteration p: eight consecutive tile rows of one
   // tile column
   auto coordB = [&](int i, int p, int& gcol, int& grow0, int& sl, int& sub, int& c_in) {
@@ -634,12 +633,11 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
     gcol = col0 + tc;
   };
 
-  auto block = [&](auto i_c) {
+  // Global inputs of block i (the iterate or A, and the weights: pass A
+  // coordinates for a wide apply, pass B for a tall one), issued one block
+  // ahead so that their latency overlaps the previous block's stores.
+  auto load_in = [&](auto i_c, Raw8 (&xin)[kEpIt], Raw8 (&win)[kEpIt]) {
     constexpr int i = decltype(i_c)::value;
-    // global inputs of both passes, issued before the staging so that their
-    // latency overlaps it (the weights: pass A for a wide apply, pass B for
-    // a tall one)
-    Raw8 xin[kEpIt], win[kEpIt];
 #pragma unroll
     for (int p = 0; p < kEpIt; ++p) {
       int grow, gcol, sl, r_in, c_in;
@@ -656,22 +654,31 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
           win[p] = load_raw8<E>(W + static_cast<size_t>(bcol) * d.cols + brow0);
       }
     }
-    {
-      float* reg = slice_of(wave);
-#pragma unroll
-      for (int j = 0; j < kBJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          reg[sidx((r >> 2) * 8 + lhalf * 4 + (r & 3), j * 32 + lrow)] = acc[i][j][r];
-    }
-    __syncthreads();
+  };
 
+  // This wave's accumulators of row block i (64 x 256 over the workgroup)
+  // into staging half h.  i is a compile-time constant in these helpers so
+  // that acc stays in registers.
+  auto stage_acc = [&](auto i_c, int h) {
+    constexpr int i = decltype(i_c)::value;
+    float* reg = slice_of(wave, h);
+#pragma unroll
+    for (int j = 0; j < kBJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        reg[sidx((r >> 2) * 8 + lhalf * 4 + (r & 3), j * 32 + lrow)] = acc[i][j][r];
+  };
+
+  // Passes A and B of block i, staged in half h (after a barrier that
+  // follows its staging).
+  auto passes = [&](auto i_c, int h, const Raw8 (&xin)[kEpIt], const Raw8 (&win)[kEpIt]) {
+    constexpr int i = decltype(i_c)::value;
     // Pass A: row-major, eight consecutive columns per thread.
 #pragma unroll
     for (int p = 0; p < kEpIt; ++p) {
       int grow, gcol, sl, r_in, c_in;
       coordA(i, p, grow, gcol, sl, r_in, c_in);
-      float* slice = slice_of(sl);
+      float* slice = slice_of(sl, h);
       float* src_lo = slice + sidx(r_in, c_in);
       float* src_hi = slice + sidx(r_in, c_in + 4);
       const float4 lo = *reinterpret_cast<const float4*>(src_lo);
@@ -725,7 +732,7 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
       for (int p = 0; p < kEpIt; ++p) {
         int gcol, grow0, sl, sub, c_in;
         coordB(i, p, gcol, grow0, sl, sub, c_in);
-        const float* slice = slice_of(sl);
+        const float* slice = slice_of(sl, h);
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = slice[sidx(sub * 8 + e, c_in)];
@@ -746,12 +753,32 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
         }
       }
     }
-    __syncthreads();
   };
-  block(std::integral_constant<int, 0>{});
-  block(std::integral_constant<int, 1>{});
-  block(std::integral_constant<int, 2>{});
-  block(std::integral_constant<int, 3>{});
+
+  // Block i + 1 is loaded and staged (half (i + 1) % 2) before block i's
+  // passes read half i % 2; one barrier per block then both frees half i % 2
+  // for block i + 2 and publishes half (i + 1) % 2.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  Raw8 xa[kEpIt], wa[kEpIt], xb[kEpIt], wb[kEpIt];
+  load_in(I0{}, xa, wa);
+  stage_acc(I0{}, 0);
+  __syncthreads();
+  load_in(I1{}, xb, wb);
+  stage_acc(I1{}, 1);
+  passes(I0{}, 0, xa, wa);
+  __syncthreads();
+  load_in(I2{}, xa, wa);
+  stage_acc(I2{}, 0);
+  passes(I1{}, 1, xb, wb);
+  __syncthreads();
+  load_in(I3{}, xb, wb);
+  stage_acc(I3{}, 1);
+  passes(I2{}, 0, xa, wa);
+  __syncthreads();
+  passes(I3{}, 1, xb, wb);
 }
 
 }  // namespace mfsdp
