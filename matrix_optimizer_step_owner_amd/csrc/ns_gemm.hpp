@@ -336,25 +336,22 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
   // Each wave issues global_load_lds_dwordx4: lane l's 16 bytes land at
   // LDS base + 16*l, so the lane picks the global chunk that belongs at that
   // swizzled position.  K-contiguous panels: 256 rows x 4 chunks of 16 bytes,
-  // chunk c of row r stored at r*4 + (c ^ kswz(r)).  The K-strided panel of
-  // the update (X, bf16): 32 k-rows x 32 chunks (256 columns), chunk c of row k
-  // at k*32 + (c ^ 4*(k & 3)); fp32: 16 k-rows x 64 chunks, unswizzled.
-  // In bf16 the update's P panel is K-strided too: B' (or A) is symmetric, so
-  // its row panel B'[row0..+256, k0..+32] equals the column panel
-  // B'[k0..+32, row0..+256], 32 rows of 512 contiguous bytes.  Each DMA
-  // request then covers whole 128-byte lines instead of 64-byte halves, which
-  // halves the L1-to-L2 requests of that panel: the texture path that feeds
-  // these DMAs is the busiest unit of the K loop on long-K products.  The
-  // polynomial's operands are both panels of the symmetric A, so in bf16 it
-  // reads both as column panels.
-  constexpr bool kPT = (kUpd || MODE == kModePoly) && V == 8;   // P panel K-strided
-  constexpr bool kQT = kUpd || (MODE == kModePoly && V == 8);   // Q panel K-strided
-  // bf16 iterates are blocked (iter_off): a K step of a Gram panel is one
-  // contiguous 16 KB block, and the update's X panel is eight 2 KB runs, one
-  // per 32-column block, kept in that order in LDS (chunk-major: column block
-  // cb, k-row kk, 16-byte unit u at cb*2048 + kk*64 + u*16).
-  constexpr bool kGB = (MODE == kModeGram || MODE == kModeSyrk) && V == 8;
-  constexpr bool kUB = kUpd && V == 8;
+  // chunk c of row r stored at r*4 + (c ^ kswz(r)).
+  // In bf16 every Newton-Schulz matrix (X, A and B') is stored in 256 x 32
+  // blocks (iter_off), so a K step of a 256-row panel is one contiguous 16 KB
+  // block: every P panel, and the Q panel of the Gram and polynomial, arrives
+  // by whole 128-byte lines (the texture path that feeds these DMAs is the
+  // busiest unit of the K loop on long-K products, and a 64-byte half line
+  // costs it as much as a whole one).  The update's Q panel (X read along K,
+  // 32 rows of 256 columns) is eight 2 KB runs, one per 32-column block, kept
+  // in that order in LDS (column block cb, k-row kk, 16-byte unit u at
+  // cb*2048 + kk*64 + u*16) and read with the transposing LDS load.  fp32
+  // matrices are row-major: K-contiguous panels read 64-byte row pieces, and
+  // the update's X panel is 16 k-rows x 64 chunks, unswizzled.
+  constexpr bool kPB = V == 8;                   // P: row panel of a blocked matrix
+  constexpr bool kQB = V == 8 && !kUpd;          // Q: row panel of a blocked matrix
+  constexpr bool kQT = kUpd;                     // Q read along K (the update's X)
+  constexpr bool kUB = kUpd && V == 8;           // ... from the blocked iterate
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> kWaveRowLog2, wc = wave & (kNsWaves / 2 - 1);
@@ -371,13 +368,13 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
     const int u = wave * (kPPW * 64) + (q % kPPW) * 64 + lane;
     const int ld = q < kPPW ? ldp : ldq;
     const int r0 = q < kPPW ? row0 : col0;
-    if (kGB) {
+    if (q < kPPW ? kPB : kQB) {
       const int row = u >> 2, c = (u & 3) ^ kswz(row);
       doff[q] = static_cast<uint32_t>(((row << 5) + c * V) * sizeof(S));
     } else if (q >= kPPW && kUB) {
       const int cb = u >> 7, kk = (u >> 2) & 31, c = u & 3;
       doff[q] = static_cast<uint32_t>(((cb << 13) + (kk << 5) + c * V) * sizeof(S));
-    } else if (!(q < kPPW ? kPT : kQT)) {
+    } else if (!(q < kPPW ? false : kQT)) {
       const int row = u >> 2, c = (u & 3) ^ kswz(row);
       doff[q] = static_cast<uint32_t>((static_cast<size_t>(r0 + row) * ld + c * V) * sizeof(S));
     } else {
@@ -393,16 +390,15 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
   auto dma_piece = [&](auto stage_c, int k0, int q) {
     constexpr int stage = decltype(stage_c)::value;
     const uint4* sbuf = stage == 0 ? st0 : stage == 1 ? st1 : stage == 2 ? st2 : st3;
-    // block (r / 256, c / 32) of a blocked iterate with row length ld
+    // block (r / 256, c / 32) of a blocked matrix with row length ld
     auto blk = [](int r, int c, int ld) {
       return static_cast<size_t>((r >> 8) * (ld >> 5) + (c >> 5)) << 13;
     };
     const char* base;
-    if (kGB)
-      base = reinterpret_cast<const char*>((q < kPPW ? P : Q) +
-                                           blk(q < kPPW ? row0 : col0, k0, q < kPPW ? ldp : ldq));
-    else if (q < kPPW)
-      base = reinterpret_cast<const char*>(kPT ? P + static_cast<size_t>(k0) * ldp : P + k0);
+    if (q < kPPW)
+      base = reinterpret_cast<const char*>(kPB ? P + blk(row0, k0, ldp) : P + k0);
+    else if (kQB)
+      base = reinterpret_cast<const char*>(Q + blk(col0, k0, ldq));
     else if (!kQT)
       base = reinterpret_cast<const char*>(Q + k0);
     else if (kUB)
@@ -419,23 +415,18 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
   // (bf16: K = 8*(2s + l/32) .. +8) of output row l%32 of each 32-row block.
   // Read piece p: 0..3 the P fragments fa[i]; then the Q fragments (NT: one
   // piece per fb[j]; bf16 update: two transposing reads per fb[j]).
-  constexpr int kPReads = kPT ? 8 : 4;
+  constexpr int kPReads = 4;
   constexpr int kReadPieces = kPReads + ((kQT && V == 8) ? 2 * kBJ : kBJ);
-  // Transposing read of half r of the fragment of a K-strided bf16 panel
-  // whose 32 columns start at n_base: within each 16-lane group, lane i points
-  // at k-row kb + i/4, columns n0 + 4*(i%4) .. +4; lane j receives column
-  // n0 + j at k-rows kb .. kb+3.
-  // k-row-major panels (a row-major source: 512-byte k-rows, 16-byte units
-  // XOR-swizzled by 4*(kk & 3)) or chunk-major ones (the blocked iterate of
-  // the update; consecutive k-rows of a column block are 64 bytes apart and
-  // need no swizzle).
-  auto tr_read = [&](const uint4* panel, int s, int n_base, int r, uint4& f, auto chunk_c) {
-    constexpr bool chunk = decltype(chunk_c)::value;
+  // Transposing read of half r of the fragment of the update's X panel
+  // (chunk-major: consecutive k-rows of a column block are 64 bytes apart and
+  // need no swizzle) whose 32 columns start at n_base: within each 16-lane
+  // group, lane i points at k-row kb + i/4, columns n0 + 4*(i%4) .. +4; lane j
+  // receives column n0 + j at k-rows kb .. kb+3.
+  auto tr_read = [&](const uint4* panel, int s, int n_base, int r, uint4& f) {
     const int il = lane & 15;
     const int n = n_base + 16 * ((lane >> 4) & 1) + 4 * (il & 3);
     const int kk = 16 * s + 8 * lhalf + 4 * r + (il >> 2);
-    const int byte = chunk ? (n >> 5) * 2048 + kk * 64 + (((n >> 3) & 3) << 4) + ((n & 7) << 1)
-                           : kk * 512 + (((n >> 3) ^ (4 * (kk & 3))) << 4) + ((n & 7) << 1);
+    const int byte = (n >> 5) * 2048 + kk * 64 + (((n >> 3) & 3) << 4) + ((n & 7) << 1);
     const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (MFSDP_LDS v4i16_t*)(reinterpret_cast<const char*>(panel) + byte));
     const uint32_t w0 = static_cast<uint16_t>(t[0]) |
@@ -453,13 +444,8 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
   auto read_piece = [&](const uint4* buf, int s, int p, uint4 (&fa)[4], uint4 (&fb)[kBJ]) {
     const int c = 2 * s + lhalf;
     if (p < kPReads) {
-      if constexpr (kPT) {
-        tr_read(buf, s, wr * 128 + (p >> 1) * 32, p & 1, fa[p >> 1],
-                std::integral_constant<bool, false>{});
-      } else {
-        const int row = wr * 128 + p * 32 + lrow;
-        fa[p] = buf[row * 4 + (c ^ kswz(row))];
-      }
+      const int row = wr * 128 + p * 32 + lrow;
+      fa[p] = buf[row * 4 + (c ^ kswz(row))];
       return;
     }
     const uint4* qp = buf + PANEL;
@@ -469,8 +455,7 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
       const int row = wc * kWaveCols + j * 32 + lrow;
       fb[j] = qp[row * 4 + (c ^ kswz(row))];
     } else if constexpr (V == 8) {
-      tr_read(qp, s, wc * kWaveCols + (q >> 1) * 32, q & 1, fb[q >> 1],
-              std::integral_constant<bool, kUB>{});
+      tr_read(qp, s, wc * kWaveCols + (q >> 1) * 32, q & 1, fb[q >> 1]);
     } else {
       const int j = q;
       const float* qf = reinterpret_cast<const float*>(qp);
@@ -643,8 +628,7 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
       int grow, gcol, sl, r_in, c_in;
       coordA(i, p, grow, gcol, sl, r_in, c_in);
       if (MODE != kModeGram && MODE != kModeSyrk && !(kUpd && ep.fold))
-        xin[p] = load_raw8<E>(ein + (kUpd ? iter_off<E>(grow, gcol, ldo)
-                                          : static_cast<size_t>(grow) * ldo + gcol));
+        xin[p] = load_raw8<E>(ein + iter_off<E>(grow, gcol, ldo));
       if (wide_apply && vec && grow < d.m && gcol + 8 <= d.n)
         win[p] = load_raw8<E>(W + static_cast<size_t>(grow) * d.cols + gcol);
       if constexpr (tall_apply && V == 8) {   // fp32: loaded in pass B (registers)
@@ -684,8 +668,7 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
       const float4 lo = *reinterpret_cast<const float4*>(src_lo);
       const float4 hi = *reinterpret_cast<const float4*>(src_hi);
       float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      const size_t goff = kUpd ? iter_off<E>(grow, gcol, ldo)
-                               : static_cast<size_t>(grow) * ldo + gcol;
+      const size_t goff = iter_off<E>(grow, gcol, ldo);
       if (MODE == kModeGram) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= alpha;
@@ -739,7 +722,7 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
         if constexpr (MODE == kModeSyrk) {
           syrk_acc8(static_cast<float*>(d.A), d.m, gcol, grow0, v, ep.a, ep.b);
         } else if constexpr (sym) {
-          store8<E>(out + static_cast<size_t>(gcol) * ldo + grow0, v);
+          store8<E>(out + iter_off<E>(gcol, grow0, ldo), v);
         } else if (tall_apply && gcol < d.n && grow0 < d.m) {
           const size_t uo = static_cast<size_t>(gcol) * d.cols + grow0;
           if (vec && grow0 + 8 <= d.m) {
