@@ -2,21 +2,23 @@
 //
 // One Newton-Schulz iteration on a wide m x n iterate X is three grouped
 // launches over every owned matrix:
-//   gram    A = alpha X X^T          (upper 256x256 tiles, mirrored store)
-//   poly    B = b A + c A A          (A symmetric, so A A = A A^T: same core)
-//   update  X' = alpha (a X + B X)   (last iteration applies W instead)
-// alpha folds the Frobenius normalization into the first iteration: the
-// first gram uses the un-normalized U with alpha = s^2 and the first update
-// alpha = s, where s = 1 / (||U||_F + eps).
+//   gram    A = alpha X X^T              (upper 256x256 tiles, mirrored store)
+//   poly    B' = a I + b A + c A A       (A symmetric, so A A = A A^T: same core)
+//   update  X' = alpha B' X              (last iteration applies W instead)
+// (with c = 0 the poly launch is skipped and the update computes
+// X' = alpha (a X + b A X)).  alpha folds the Frobenius normalization into
+// the first iteration: the first gram uses the un-normalized U with
+// alpha = s^2 and the first update alpha = s, where s = 1 / (||U||_F + eps).
 //
 // Kernel shape: one workgroup per 256x256 output tile, 8 waves, each a
 // 128x64 block of 4x2 MFMA 32x32 tiles.  Operand panels (one K step: 64
 // bf16 or 32 fp32 per row) go from global memory straight into LDS
-// (global_load_lds_dwordx4, no register staging) in four 32 KB stages;
-// rows are XOR-swizzled in 16-byte chunks so fragment reads are free of bank
-// conflicts.  The update's K-strided operand X keeps its row-major layout in
-// LDS and is read with the gfx950 transposing LDS load (ds_read_b64_tr_b16),
-// which hands each lane four consecutive K values of its own column.
+// (global_load_lds_dwordx4, no register staging) in four 32 KB stages; in
+// bf16 every panel comes from a blocked matrix (iter_off) by whole 128-byte
+// lines.  K-contiguous panel rows are XOR-swizzled in 16-byte chunks so
+// fragment reads are free of bank conflicts.  The update's X, read along K,
+// is read with the gfx950 transposing LDS load (ds_read_b64_tr_b16), which
+// hands each lane four consecutive K values of its own column.
 #pragma once
 
 #include <type_traits>
