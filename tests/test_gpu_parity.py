@@ -437,3 +437,22 @@ def test_small_matrix_variants(variant):
     else:
         hp["nesterov"] = False
     run_and_check(Ws, Gs, Ms, hp, torch.float32, label=f"small {variant}")
+
+
+EXTREME = [(200, 8192), (8192, 200), (129, 2000), (700, 3000), (3000, 700), (1100, 1300)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_extreme_aspect_ratios(dtype):
+    # Tiled-path matrices far from square: one 256-row panel with a K = 8192
+    # Gram and 32 update tile columns (200 x 8192 and its transpose), m just
+    # above the small-matrix limit (129 x 2000), and matrices with several
+    # ragged row panels in both directions.  Every matrix against the oracle,
+    # and each one stepped alone bitwise equal to its result in the list.
+    Ws, Gs, Ms = wlm.random_matrix_inputs(EXTREME, dtype, seed=51)
+    hp = muon_hparams()
+    st, _ = run_and_check(Ws, Gs, Ms, hp, dtype, label=f"extreme {dtype}")
+    for i in range(len(EXTREME)):
+        one = GpuStep([Ws[i]], [Gs[i]], [Ms[i]])
+        one.run(**hp)
+        assert torch.equal(one.W[0], st.W[i]) and torch.equal(one.U[0], st.U[i]), i
