@@ -104,20 +104,28 @@ hipError_t drain_timing() {
 template <class F>
 hipError_t launch(int kind, hipStream_t stream, F&& f) {
   hipEvent_t a = nullptr, b = nullptr;
+  // events taken but not recorded as a pair go back to the free list
+  auto give_back = [&] {
+    if (a) g_timing.free_events.push_back(a);
+    if (b) g_timing.free_events.push_back(b);
+  };
   if (g_timing.enabled) {
     hipError_t e = take_event(&a);
     if (e == hipSuccess) e = take_event(&b);
     if (e == hipSuccess) e = hipEventRecord(a, stream);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) {
+      give_back();
+      return e;
+    }
   }
   f();
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (g_timing.enabled) {
-    e = hipEventRecord(b, stream);
-    if (e != hipSuccess) return e;
-    g_timing.pending.push_back({kind, a, b});
+  if (e == hipSuccess && g_timing.enabled) e = hipEventRecord(b, stream);
+  if (e != hipSuccess) {
+    give_back();
+    return e;
   }
+  if (g_timing.enabled) g_timing.pending.push_back({kind, a, b});
   return hipSuccess;
 }
 
