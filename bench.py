@@ -20,7 +20,10 @@ from a second pass of the same K steps right after the timed region, with the
 Newton-Schulz work on ONE stream (MFSDP_NS_GROUPS=1) so that no two kernels of
 the library overlap; the library records hipEvents around each of its launches
 on the launch stream, and ``achieved`` is the kernel's algorithmic flops (or
-bytes) per launch over its average launch duration.  ``kernels`` holds the
+bytes) per launch over its average launch duration.  A Newton-Schulz kernel is
+priced against the MFMA peak when its flops per algorithmic byte (operands read
+once, results written once) reach the ridge of the chip (peak flops over 8 TB/s),
+else against HBM; ``mfma_frac`` and ``hbm_frac`` give both.  ``kernels`` holds the
 same per-kind figures.  ``traffic`` is the kernel's measured HBM bytes per
 launch (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy) read from
 profiles/, or null when the kernel sources changed since it was measured.
@@ -80,6 +83,42 @@ def ns_flops_by_kind(shapes):
         p += m * m * (m + 1)
         u += 2 * m * m * n
     return {"gram": g, "poly": p, "update": u}
+
+
+def ns_bytes_by_kind(shapes, es):
+    """Algorithmic HBM bytes of ONE launch of each Newton-Schulz kernel kind,
+    every operand read once and every result written once (storage dtype of
+    es bytes): gram reads X (m x n) and writes A (m x m); poly reads A and
+    writes B'; update reads B' and X and writes X'.  One iteration moves
+    3mn + 4m^2 elements.
+    """
+    g = p = u = 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        g += (m * n + m * m) * es
+        p += 2 * m * m * es
+        u += (m * m + 2 * m * n) * es
+    return {"gram": g, "poly": p, "update": u}
+
+
+def ns_roofline(flops, nbytes, sec, peak_tflops):
+    """Roofline of one Newton-Schulz launch: algorithmic flops and bytes per
+    launch over its duration.  Its bound is the MFMA peak when the launch's
+    intensity (flops per algorithmic byte) is at or above the chip's ridge,
+    else HBM; both fractions are given either way."""
+    ai = flops / nbytes
+    ridge = peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9)
+    tflops = flops / sec / 1e12
+    gbs = nbytes / sec / 1e9
+    if ai >= ridge:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": peak_tflops, "unit": "TFLOP/s",
+                "frac": tflops / peak_tflops}
+    else:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS}
+    roof.update({"flop_per_byte": round(ai, 1), "ridge_flop_per_byte": round(ridge, 1),
+                 "mfma_frac": tflops / peak_tflops, "hbm_frac": gbs / PEAK_HBM_GBS})
+    return roof
 
 
 def elementwise_bytes(shapes, es, tail_n):
@@ -396,9 +435,9 @@ def main():
         roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS}
     elif dominant in flops:
-        achieved = flops[dominant] / (per_kind[dominant]["avg_ms"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak}
+        nsb = ns_bytes_by_kind([s for s in shapes if s not in small], es)
+        roof = ns_roofline(flops[dominant], nsb[dominant], per_kind[dominant]["avg_ms"] * 1e-3,
+                           peak)
     else:
         achieved = ew[dominant] / (per_kind[dominant]["avg_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
