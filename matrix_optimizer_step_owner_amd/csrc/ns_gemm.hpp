@@ -18,7 +18,11 @@
 // lines.  K-contiguous panel rows are XOR-swizzled in 16-byte chunks so
 // fragment reads are free of bank conflicts.  The update's X, read along K,
 // is read with the gfx950 transposing LDS load (ds_read_b64_tr_b16), which
-// hands each lane four consecutive K values of its own column.
+// hands each lane four consecutive K values of its own column.  The
+// epilogue stages the accumulators through the freed stages in 64-row
+// blocks for 16-byte, whole-line stores: in bf16, column-major and already
+// rounded, where the output is a plain scaling (Gram, folded update); in
+// fp32 otherwise.
 #pragma once
 
 #include <type_traits>
@@ -594,6 +598,107 @@ __global__ __launch_bounds__(kNsThreads) void ns_gemm_kernel(
   S* W = static_cast<S*>(d.W);
   const int ldo = sym ? d.m_pad : d.n_pad;
   const bool vec = d.vec_ok != 0;
+
+  // bf16 outputs that are a plain scaling of the accumulators -- the Gram,
+  // and the update when the polynomial is folded -- are scaled and rounded in
+  // registers (bitwise the values the fp32 staging below would store) and
+  // staged in bf16, column-major: half the LDS bytes, four consecutive rows
+  // of a column per 8-byte write.  A staging half is two quarters of 128 tile
+  // columns x 64 staged rows (pitch kQP elements; staged row wr*32 + rr is
+  // tile row wr*128 + 32*i + rr of block i), quarter q of half h in stage
+  // array 2h + q.  Row segments are read back with the transposing LDS load
+  // (16 lanes: 16 consecutive rows, 4 columns each) and the mirror's with
+  // plain 8-byte loads; every wave store writes 16 rows x 64 bytes of one
+  // 256 x 32 block, i.e. eight whole lines.
+  constexpr bool kB16Stage = V == 8 && (MODE == kModeGram || MODE == kModeUpdate);
+  if constexpr (kB16Stage) {
+    if (MODE == kModeGram || ep.fold) {
+      constexpr int kQP = 68;   // staged column pitch (bf16): 8-byte aligned, 34 banks
+      auto quarter = [&](int h, int q) -> uint16_t* {
+        const int sa = 2 * h + q;
+        return reinterpret_cast<uint16_t*>(sa == 0 ? st0 : sa == 1 ? st1 : sa == 2 ? st2 : st3);
+      };
+      auto stage16 = [&](auto i_c, int h) {
+        constexpr int i = decltype(i_c)::value;
+        uint16_t* qb = quarter(h, wc >> 1);
+#pragma unroll
+        for (int j = 0; j < kBJ; ++j) {
+          const int cl = (wc & 1) * kWaveCols + j * 32 + lrow;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const uint2 pk = make_uint2(
+                pack_bf16x2(alpha * acc[i][j][4 * q4], alpha * acc[i][j][4 * q4 + 1]),
+                pack_bf16x2(alpha * acc[i][j][4 * q4 + 2], alpha * acc[i][j][4 * q4 + 3]));
+            *reinterpret_cast<uint2*>(qb + cl * kQP + wr * 32 + q4 * 8 + lhalf * 4) = pk;
+          }
+        }
+      };
+      const int g = lane >> 4, jl = lane & 15;
+      // row segments: unit u = (16 staged rows rg, one 32-column block cb)
+      auto pass_rows = [&](auto i_c, int h) {
+        constexpr int i = decltype(i_c)::value;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int u = p * kNsWaves + wave;
+          const int rg = u >> 3, cb = u & 7;
+          const char* qb = reinterpret_cast<const char*>(quarter(h, cb >> 2));
+          const int cq = (cb & 3) * 32 + 8 * g;
+          uint32_t w[4];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int byte = ((cq + 4 * hh + (jl >> 2)) * kQP + rg * 16 + 4 * (jl & 3)) * 2;
+            const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (MFSDP_LDS v4i16_t*)(qb + byte));
+            w[2 * hh] = static_cast<uint16_t>(t[0]) |
+                        (static_cast<uint32_t>(static_cast<uint16_t>(t[1])) << 16);
+            w[2 * hh + 1] = static_cast<uint16_t>(t[2]) |
+                            (static_cast<uint32_t>(static_cast<uint16_t>(t[3])) << 16);
+          }
+          const int sr = rg * 16 + jl;
+          const int grow = row0 + (sr >> 5) * 128 + i * 32 + (sr & 31);
+          const int gcol = col0 + cb * 32 + 8 * g;
+          gst<uint4>(out + iter_off<E>(grow, gcol, ldo), make_uint4(w[0], w[1], w[2], w[3]));
+        }
+      };
+      // mirror segments: unit u = (16 tile columns cg, one 32-row half wrr)
+      auto pass_mirror = [&](auto i_c, int h) {
+        constexpr int i = decltype(i_c)::value;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int u = p * kNsWaves + wave;
+          const int cg = u >> 1, wrr = u & 1;
+          const int c = cg * 16 + jl;
+          const uint16_t* src = quarter(h, c >> 7) + (c & 127) * kQP + wrr * 32 + 8 * g;
+          const uint2 lo = *reinterpret_cast<const uint2*>(src);
+          const uint2 hi = *reinterpret_cast<const uint2*>(src + 4);
+          const int grow_m = row0 + wrr * 128 + i * 32 + 8 * g;
+          gst<uint4>(out + iter_off<E>(col0 + c, grow_m, ldo), make_uint4(lo.x, lo.y, hi.x, hi.y));
+        }
+      };
+      using J0 = std::integral_constant<int, 0>;
+      using J1 = std::integral_constant<int, 1>;
+      using J2 = std::integral_constant<int, 2>;
+      using J3 = std::integral_constant<int, 3>;
+      // block i + 1 is staged while block i is stored, as below
+      stage16(J0{}, 0);
+      __syncthreads();
+      stage16(J1{}, 1);
+      pass_rows(J0{}, 0);
+      if (mirror) pass_mirror(J0{}, 0);
+      __syncthreads();
+      stage16(J2{}, 0);
+      pass_rows(J1{}, 1);
+      if (mirror) pass_mirror(J1{}, 1);
+      __syncthreads();
+      stage16(J3{}, 1);
+      pass_rows(J2{}, 0);
+      if (mirror) pass_mirror(J2{}, 0);
+      __syncthreads();
+      pass_rows(J3{}, 1);
+      if (mirror) pass_mirror(J3{}, 1);
+      return;
+    }
+  }
 
   // pass A coordinates of iteration p: tile row, tile column, staged slice
   auto coordA = [&](int i, int p, int& grow, int& gcol, int& sl, int& r_in, int& c_in) {
