@@ -171,6 +171,10 @@ def counter_table(pmc_csvs: List[str], calib: Dict[str, float]) -> List[dict]:
                 row["mfma_busy_pct"] = 100.0 * row["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD)
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in row and dur_s > 0:
             row["mfma_tflops"] = row["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / dur_s / 1e12
+        if "TCC_HIT_sum" in row and "TCC_MISS_sum" in row:
+            req = row["TCC_HIT_sum"] + row["TCC_MISS_sum"]
+            if req > 0:
+                row["l2_hit_pct"] = 100.0 * row["TCC_HIT_sum"] / req
         for cn in ("FETCH_SIZE", "WRITE_SIZE"):
             if cn in row and cn in calib and dur_s > 0:
                 row[cn.lower() + "_mb"] = row[cn] * 1024.0 / calib[cn] / 1e6
@@ -200,9 +204,10 @@ def format_counters(rows: List[dict], commands: List[str], calib: Dict[str, floa
             f"(GRBM_GUI_ACTIVE per XCD x {N_SIMD} SIMDs).  GRBM_GUI_ACTIVE spans the profiler's",
             "dispatch window, some microseconds longer than the kernel, so both are given only",
             f"for kernels of {MIN_GRBM_US:.0f} us or more and overstate sclk (understate busy) by",
-            "about that window over the duration.", "",
+            "about that window over the duration.  L2 hit% = TCC_HIT_sum / (TCC_HIT_sum +",
+            "TCC_MISS_sum), in requests.", "",
             f"{'kind':12s} {'disp':>5s} {'avg us':>9s} {'sclk GHz':>9s} {'MFMA busy%':>10s} "
-            f"{'MFMA TF/s':>10s} {'fetch MB':>10s} {'write MB':>10s} {'HBM GB/s':>9s}"]
+            f"{'MFMA TF/s':>10s} {'fetch MB':>10s} {'write MB':>10s} {'HBM GB/s':>9s} {'L2 hit%':>8s}"]
     for r in rows:
         def f(key, fmt):
             return format(r[key], fmt) if key in r else "-"
@@ -210,7 +215,7 @@ def format_counters(rows: List[dict], commands: List[str], calib: Dict[str, floa
         out.append(f"{r['kind']:12s} {r['dispatches']:5d} {r['avg_us']:9.2f} {f('sclk_ghz', '9.2f'):>9s} "
                    f"{f('mfma_busy_pct', '10.1f'):>10s} {f('mfma_tflops', '10.1f'):>10s} "
                    f"{f('fetch_size_mb', '10.1f'):>10s} {f('write_size_mb', '10.1f'):>10s} "
-                   f"{format(hbm, '9.0f') if hbm else '-':>9s}")
+                   f"{format(hbm, '9.0f') if hbm else '-':>9s} {f('l2_hit_pct', '8.1f'):>8s}")
     return "\n".join(out) + "\n"
 
 
