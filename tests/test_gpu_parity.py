@@ -456,3 +456,21 @@ def test_extreme_aspect_ratios(dtype):
         one = GpuStep([Ws[i]], [Gs[i]], [Ms[i]])
         one.run(**hp)
         assert torch.equal(one.W[0], st.W[i]) and torch.equal(one.U[0], st.U[i]), i
+
+
+def _random_shapes(n, seed, lo=1, hi=1500):
+    rng = np.random.default_rng(seed)
+    dims = np.exp(rng.uniform(np.log(lo), np.log(hi), size=(n, 2))).astype(int)
+    return [(int(r), int(c)) for r, c in np.clip(dims, lo, hi)]
+
+
+def test_random_shapes_fp32():
+    # Sixteen seeded shapes, log-uniform in 1..1500 on each side: small-path
+    # and tiled matrices, wide, tall and ragged in both directions, in one
+    # grouped call, every matrix against the oracle at the fp32 bar.  (In
+    # bf16 the rounding of the iterates alone can approach the 2e-2 bar for
+    # matrices whose singular values share a narrow band, so the random
+    # sweep uses the dtype whose bar every shape meets.)
+    shapes = _random_shapes(16, seed=61)
+    Ws, Gs, Ms = wlm.random_matrix_inputs(shapes, torch.float32, seed=62)
+    run_and_check(Ws, Gs, Ms, muon_hparams(), torch.float32, label="random fp32")
