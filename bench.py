@@ -27,6 +27,11 @@ else against HBM; ``mfma_frac`` and ``hbm_frac`` give both.  ``kernels`` holds t
 same per-kind figures.  ``traffic`` is the kernel's measured HBM bytes per
 launch (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy) read from
 profiles/, or null when the kernel sources changed since it was measured.
+``mfma_loop`` is the sustained bf16 MFMA rate of the same GPU with no memory
+traffic (mfsdp_mfma_probe, timed in the same run): under sustained MFMA load
+the clock settles well below the one at which the dense peak is quoted, so
+``roofline.frac_of_mfma_loop`` gives the dominant kernel against what the chip
+sustains, beside ``frac`` against the published peak.
 ``cpu_baseline`` is the float64 oracle on a bounded sample of the same
 workload on the host cores.
 """
@@ -119,6 +124,33 @@ def ns_roofline(flops, nbytes, sec, peak_tflops):
     roof.update({"flop_per_byte": round(ai, 1), "ridge_flop_per_byte": round(ridge, 1),
                  "mfma_frac": tflops / peak_tflops, "hbm_frac": gbs / PEAK_HBM_GBS})
     return roof
+
+
+def mfma_ceiling(dev, reps=5, iters=20000, blocks=1024):
+    """Sustained bf16 MFMA rate of this GPU with no memory traffic
+    (mfsdp_mfma_probe, each launch timed alone with hipEvents on the current
+    stream): the practical ceiling under the power cap, reported beside the
+    published peak.  Median and maximum TFLOP/s over `reps` launches."""
+    import matrix_optimizer_step_owner_amd as mf
+    out = torch.empty(blocks * 8, dtype=torch.float32, device=dev)
+    flops = blocks * 8 * 8 * iters * 2.0 * 32 * 32 * 16
+    mf.mfma_probe(out, iters)
+    torch.cuda.synchronize()
+    tf = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mf.mfma_probe(out, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        tf.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("MFMA probe produced non-finite sums")
+    tf.sort()
+    return {"tflops_median": round(tf[len(tf) // 2], 1), "tflops_max": round(tf[-1], 1),
+            "reps": reps, "blocks": blocks, "iters": iters,
+            "flops_per_launch": flops}
 
 
 def elementwise_bytes(shapes, es, tail_n):
@@ -314,6 +346,12 @@ def main():
     ap.add_argument("--adamw-elements", type=int, default=0,
                     help="measure mfsdp_adamw_tail alone on a packed fp32 tail of this many "
                          "elements instead of the Muon step")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="measure only the sustained bf16 MFMA rate with no memory traffic "
+                         "(mfsdp_mfma_probe) and print it")
+    ap.add_argument("--mfma-iters", type=int, default=20000,
+                    help="iterations per wave of each MFMA-ceiling launch (20000: ~30 ms, "
+                         "long enough for the clock to settle)")
     ap.add_argument("--ns-groups", type=int, default=0,
                     help="Newton-Schulz stream groups in the timed region (0: the library's "
                          "own choice)")
@@ -336,6 +374,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.mfma_ceiling:
+        print(json.dumps({"mfma_loop": mfma_ceiling(dev, reps=max(args.steps, 1),
+                                                     iters=args.mfma_iters)}), flush=True)
+        return
     if args.adamw_elements > 0:
         adamw_bench(args, dev)
         return
@@ -456,6 +498,13 @@ def main():
                 and tr.get("source_sha256") == profiling.kernel_source_hash(dominant)):
             roof["traffic"] = tr.get("bytes_per_launch")
 
+    # the practical MFMA ceiling of this GPU, measured in the same run
+    mfma_loop = None
+    if roof["bound"] == "mfma" and wl.dtype == torch.bfloat16:
+        mfma_loop = mfma_ceiling(dev, iters=args.mfma_iters)
+        roof["mfma_loop_tflops"] = mfma_loop["tflops_median"]
+        roof["frac_of_mfma_loop"] = roof["achieved"] / mfma_loop["tflops_median"]
+
     kernels = {}
     for k, v in per_kind.items():
         e = {"avg_ms": round(v["avg_ms"], 5), "ms_per_step": round(v["ms_per_step"], 5)}
@@ -493,6 +542,7 @@ def main():
         "cold_cache": {"reps": len(cold), "flush_bytes": FLUSH_BYTES,
                        "ms_median": round(cold[len(cold) // 2], 4), "ms_min": round(cold[0], 4)},
         "roofline": roof,
+        "mfma_loop": mfma_loop,
         "setup_s": {"generate": round(setup_gen_s, 1), "generate_and_upload": round(setup_s, 1)},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.workload, sample,
                                                                       args.cpu_budget),

@@ -358,6 +358,21 @@ mfsdp_status_t mfsdp_timing_reset(void);
 mfsdp_status_t mfsdp_timing_read(mfsdp_kernel_kind_t kind, double* total_ms,
                                  int64_t* launches);
 
+/*
+ * Measurement only: the sustained bf16 MFMA rate of this GPU with no memory
+ * traffic, the practical ceiling for the Newton-Schulz products (under
+ * sustained MFMA load the clock settles below the one at which the dense peak
+ * is quoted).  Launches `blocks` workgroups of 8 waves on `stream`; each wave
+ * issues 8 * iters v_mfma_f32_32x32x16_bf16 (32768 flops each) on register
+ * operands and writes one float to out[8 * block + wave] (device, blocks * 8
+ * floats, 4-byte aligned).  The caller times the launch (for example with
+ * hipEvents on `stream`).  Errors: MFSDP_ERR_INVALID_ARGUMENT (NULL or
+ * misaligned out, blocks outside [1, 65536], iters outside [1, 2^20]),
+ * MFSDP_ERR_HIP.
+ */
+mfsdp_status_t mfsdp_mfma_probe(float* out, int64_t blocks, int iters,
+                                hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

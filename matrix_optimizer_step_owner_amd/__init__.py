@@ -25,7 +25,7 @@ from ._lib import MfsdpError, NOALLOC_SCRATCH_BYTES, NS_EPS
 
 __all__ = ["muon_step", "muon_step_noalloc", "MuonStep", "adamw_tail", "muon_workspace_size",
            "default_scale", "plan_owners", "tail_layout", "tail_pack", "tail_unpack",
-           "shampoo_stats", "timing", "MfsdpError", "NS_EPS", "NOALLOC_SCRATCH_BYTES",
+           "shampoo_stats", "mfma_probe", "timing", "MfsdpError", "NS_EPS", "NOALLOC_SCRATCH_BYTES",
            "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -416,6 +416,16 @@ def tail_unpack(packed: torch.Tensor, tensors: Sequence[torch.Tensor],
     stream = torch.cuda.current_stream(packed.device).cuda_stream
     _lib.check(lib.mfsdp_tail_unpack(packed.data_ptr(), packed.numel(), ptrs, nums, offs,
                                      len(tensors), stream))
+
+
+def mfma_probe(out: torch.Tensor, iters: int) -> None:
+    """Enqueue the MFMA-only measurement kernel (mfsdp_mfma_probe) on torch's
+    current stream: out.numel() // 8 workgroups of 8 waves, 8 * iters bf16
+    MFMAs of 32768 flops per wave; out is a contiguous fp32 device tensor."""
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() % 8:
+        raise ValueError("out must be a contiguous fp32 tensor of 8 floats per workgroup")
+    stream = torch.cuda.current_stream(out.device).cuda_stream
+    _lib.check(_lib.load().mfsdp_mfma_probe(out.data_ptr(), out.numel() // 8, int(iters), stream))
 
 
 class timing:

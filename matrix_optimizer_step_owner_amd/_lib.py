@@ -28,7 +28,8 @@ EXPORTED = ("mfsdp_muon_workspace_size", "mfsdp_muon_step", "mfsdp_muon_step_noa
             "mfsdp_plan_owners", "mfsdp_tail_layout", "mfsdp_tail_pack",
             "mfsdp_tail_unpack", "mfsdp_stats_workspace_size", "mfsdp_shampoo_stats",
             "mfsdp_status_string", "mfsdp_last_error",
-            "mfsdp_timing_enable", "mfsdp_timing_reset", "mfsdp_timing_read")
+            "mfsdp_timing_enable", "mfsdp_timing_reset", "mfsdp_timing_read",
+            "mfsdp_mfma_probe")
 
 
 class MfsdpMatrix(ctypes.Structure):
@@ -123,6 +124,8 @@ def load() -> ctypes.CDLL:
         lib.mfsdp_timing_read.argtypes = [c.c_int, c.POINTER(c.c_double),
                                           c.POINTER(c.c_int64)]
         lib.mfsdp_timing_read.restype = c.c_int
+        lib.mfsdp_mfma_probe.argtypes = [c.c_void_p, c.c_int64, c.c_int, c.c_void_p]
+        lib.mfsdp_mfma_probe.restype = c.c_int
         _lib = lib
         return lib
 

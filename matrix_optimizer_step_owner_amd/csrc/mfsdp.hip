@@ -29,6 +29,7 @@
 #include "ns_gemm.hpp"
 #include "ns_small.hpp"
 #include "planner.hpp"
+#include "probe_kernels.hpp"
 #include "stats_kernels.hpp"
 #include "tail_kernels.hpp"
 
@@ -1323,6 +1324,20 @@ mfsdp_status_t mfsdp_tail_unpack(const float* packed, int64_t packed_numel, floa
   } catch (const std::exception& ex) {
     return fail(MFSDP_ERR_UNSUPPORTED, "host exception: %s", ex.what());
   }
+}
+
+mfsdp_status_t mfsdp_mfma_probe(float* out, int64_t blocks, int iters, hipStream_t stream) {
+  g_last_error.clear();
+  if (!out) return fail(MFSDP_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (blocks < 1 || blocks > (int64_t(1) << 16) || iters < 1 || iters > (1 << 20))
+    return fail(MFSDP_ERR_INVALID_ARGUMENT, "blocks=%lld iters=%d outside [1, 65536] x [1, 2^20]",
+                (long long)blocks, iters);
+  if (!aligned(out, 4)) return fail(MFSDP_ERR_INVALID_ARGUMENT, "out must be 4-byte aligned");
+  mfma_probe_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kProbeThreads), 0, stream>>>(
+      out, iters);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MFSDP_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
+  return MFSDP_OK;
 }
 
 mfsdp_status_t mfsdp_timing_enable(int enable) {

@@ -69,7 +69,8 @@ def short_name(kernel: str) -> str:
         return _NS_MODES[m.group(2)] + ("" if m.group(1) == "BF16" else "_f32")
     for key, name in (("small_ns_kernel", "small"), ("momentum_kernel", "momentum"),
                       ("norm_finalize_kernel", "norm"),
-                      ("adamw_kernel", "adamw"), ("apply_x0_kernel", "apply")):
+                      ("adamw_kernel", "adamw"), ("apply_x0_kernel", "apply"),
+                      ("mfma_probe_kernel", "mfma_loop")):
         if key in kernel:
             return name
     return ""

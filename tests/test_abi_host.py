@@ -261,3 +261,14 @@ def test_noalloc_step_refuses_a_list_beyond_its_scratch():
     assert lib.mfsdp_muon_step_noalloc(None, 0, _lib.DTYPE_BF16, float("nan"), 0.95, 1,
                                        0.01, 5, *abc, None) == 1
     assert lib.mfsdp_muon_step_noalloc(None, 0, 9, 0.02, 0.95, 1, 0.01, 5, *abc, None) == 2
+
+
+def test_mfma_probe_validation():
+    # refused before any launch (no device needed)
+    lib = _lib.load()
+    assert lib.mfsdp_mfma_probe(None, 8, 10, None) == 1
+    assert lib.mfsdp_mfma_probe(FAKE, 0, 10, None) == 1
+    assert lib.mfsdp_mfma_probe(FAKE, (1 << 16) + 1, 10, None) == 1
+    assert lib.mfsdp_mfma_probe(FAKE, 8, 0, None) == 1
+    assert lib.mfsdp_mfma_probe(FAKE + 2, 8, 10, None) == 1
+    assert b"aligned" in lib.mfsdp_last_error()

@@ -474,3 +474,12 @@ def test_random_shapes_fp32():
     shapes = _random_shapes(16, seed=61)
     Ws, Gs, Ms = wlm.random_matrix_inputs(shapes, torch.float32, seed=62)
     run_and_check(Ws, Gs, Ms, muon_hparams(), torch.float32, label="random fp32")
+
+
+def test_mfma_probe_runs_and_sums_are_finite():
+    # the measurement kernel that bench.py times as the sustained MFMA ceiling
+    dev = torch.device("cuda:0")
+    out = torch.full((16 * 8,), float("nan"), dtype=torch.float32, device=dev)
+    mf.mfma_probe(out, iters=50)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool((out > 0).all())
