@@ -201,7 +201,29 @@ def cpu_baseline(key, sample, budget_s=20.0):
             "kind": "oracle",
             "sample": f"float64 numpy oracle Muon step on {len(done)} matrices of "
                       f"{key} ({', '.join(done)}), {t_total:.1f} s, NS algorithmic flops "
-                      f"{done_flops:.3e}"}
+                      f"{done_flops:.3e}",
+            "host": host_description()}
+
+
+def host_description():
+    """CPU model and the BLAS numpy uses (the oracle's matrix products)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # older numpy: no dict form
+        pass
+    return {"cpu": model, "blas": blas}
 
 
 def stats_bench(args, wl, dev):
