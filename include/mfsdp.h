@@ -367,7 +367,8 @@ mfsdp_status_t mfsdp_timing_read(mfsdp_kernel_kind_t kind, double* total_ms,
  * operands and writes one float to out[8 * block + wave] (device, blocks * 8
  * floats, 4-byte aligned).  The caller times the launch (for example with
  * hipEvents on `stream`).  Errors: MFSDP_ERR_INVALID_ARGUMENT (NULL or
- * misaligned out, blocks outside [1, 65536], iters outside [1, 2^20]),
+ * misaligned out, blocks outside [1, 65536], iters outside [1, 2^20], or
+ * blocks * iters above 2^28, which bounds a launch to about half a second),
  * MFSDP_ERR_HIP.
  */
 mfsdp_status_t mfsdp_mfma_probe(float* out, int64_t blocks, int iters,

@@ -1332,6 +1332,10 @@ mfsdp_status_t mfsdp_mfma_probe(float* out, int64_t blocks, int iters, hipStream
   if (blocks < 1 || blocks > (int64_t(1) << 16) || iters < 1 || iters > (1 << 20))
     return fail(MFSDP_ERR_INVALID_ARGUMENT, "blocks=%lld iters=%d outside [1, 65536] x [1, 2^20]",
                 (long long)blocks, iters);
+  if (blocks * static_cast<int64_t>(iters) > (int64_t(1) << 28))
+    return fail(MFSDP_ERR_INVALID_ARGUMENT,
+                "blocks * iters = %lld exceeds 2^28 (about half a second of MFMA work)",
+                (long long)(blocks * static_cast<int64_t>(iters)));
   if (!aligned(out, 4)) return fail(MFSDP_ERR_INVALID_ARGUMENT, "out must be 4-byte aligned");
   mfma_probe_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kProbeThreads), 0, stream>>>(
       out, iters);

@@ -270,5 +270,7 @@ def test_mfma_probe_validation():
     assert lib.mfsdp_mfma_probe(FAKE, 0, 10, None) == 1
     assert lib.mfsdp_mfma_probe(FAKE, (1 << 16) + 1, 10, None) == 1
     assert lib.mfsdp_mfma_probe(FAKE, 8, 0, None) == 1
+    assert lib.mfsdp_mfma_probe(FAKE, 65536, 1 << 20, None) == 1
+    assert b"2^28" in lib.mfsdp_last_error()
     assert lib.mfsdp_mfma_probe(FAKE + 2, 8, 10, None) == 1
     assert b"aligned" in lib.mfsdp_last_error()
