@@ -483,3 +483,24 @@ def test_mfma_probe_runs_and_sums_are_finite():
     mf.mfma_probe(out, iters=50)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all()) and bool((out > 0).all())
+
+
+def _random_shapes_bf16(n, seed, lo=129, hi=1500, max_aspect=4.0):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        r, c = np.exp(rng.uniform(np.log(lo), np.log(hi), size=2)).astype(int)
+        if max(r, c) / min(r, c) <= max_aspect:
+            out.append((int(r), int(c)))
+    return out
+
+
+def test_random_shapes_bf16():
+    # Twelve seeded tiled-path shapes (129..1500 per side, aspect ratio at
+    # most 4, ragged in both directions) in one grouped bf16 call, each against
+    # the oracle at the bf16 bars.  The range keeps the rounding of the bf16
+    # iterates itself, as a CPU emulation of the defined iteration gives it
+    # for these very inputs (0.88-1.05e-2), well inside the 2e-2 bar.
+    shapes = _random_shapes_bf16(12, seed=63)
+    Ws, Gs, Ms = wlm.random_matrix_inputs(shapes, torch.bfloat16, seed=64)
+    run_and_check(Ws, Gs, Ms, muon_hparams(), torch.bfloat16, label="random bf16")
